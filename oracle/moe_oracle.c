@@ -1,0 +1,448 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle for the forward pass of one
+ * sparsely-gated Mixture-of-Experts layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this library. It shares no code, header,
+ * table or constant with the GPU library; the two are written independently
+ * from the same definitions.
+ *
+ * Sources (the pages), cited by title and section:
+ *   [Shazeer]  "Outrageously Large Neural Networks: The Sparsely-Gated
+ *              Mixture-of-Experts Layer" summary page: section "Methode (mit den
+ *              Schluesselgleichungen)" -- the layer equation, the "Noisy Top-K
+ *              Gating" equations and the "Load-Balancing-Losses" equations.
+ *   [Switch]   "Switch Transformer" dictionary page: the definition (top-1
+ *              routing) and its pseudo-implementation listing (softmax over all
+ *              experts, top-1, gate = mask * weights, per-expert dispatch).
+ *   [Tables]   "moe paper models" page, table 2: capacity factors (1.25 ST-MoE,
+ *              1/1.5/2x MegaBlocks, 2 GLaM).
+ *
+ * Where the pages leave a step open, the reading taken is stated at the
+ * function. Routing decisions (which experts a token picks, ranks, drops) are
+ * integers decided by floating-point comparisons; both this oracle and the GPU
+ * take them on fp32 logits defined bit-for-bit below (canonical order of
+ * operations), so the integer outputs must agree exactly. All other float
+ * steps are evaluated in fp64 here.
+ *
+ * Parity pins: every function is pinned by tests against closed forms,
+ * invariants, library routines or brute force (tests/test_oracle_*.py).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_RELU = 0, OR_GELU = 1 };
+
+/* ------------------------------------------------------------------------ */
+/* Element access: bf16 is widened to fp32 exactly (its bits are the high    */
+/* half of the fp32 pattern).                                                */
+/* ------------------------------------------------------------------------ */
+static float widen_bf16(uint16_t h) {
+  uint32_t u = ((uint32_t)h) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+static float elem(const void* base, int dtype, int64_t i) {
+  if (dtype == OR_BF16) return widen_bf16(((const uint16_t*)base)[i]);
+  return ((const float*)base)[i];
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* Canonical softplus.                                                       */
+/*                                                                           */
+/* [Shazeer] "Noisy Top-K Gating": the noise scale is Softplus of the noise  */
+/* projection, and it enters the logits that decide top-k. The pages fix no  */
+/* precision, so softplus is *defined* here from correctly rounded IEEE fp32 */
+/* +, -, *, /, fma, rint and ldexp only (no library transcendental), so that */
+/* the CPU and the GPU evaluate the identical function:                      */
+/*   softplus(z) = z                      for z > 20                         */
+/*               = z + log1p(exp(-|z|))   for 0 < z <= 20                    */
+/*               = log1p(exp(-|z|))       for z <= 0                         */
+/* exp(y), y <= 0: Cody-Waite reduction y = n*ln2 + r with ln2 split into a  */
+/* 12-bit-short head and a tail, then the degree-7 Taylor polynomial of e^r  */
+/* evaluated by Horner with fma, scaled by 2^n. Zero below -87.              */
+/* log1p(v), 0 <= v <= 1: log1p(v) = 2*atanh(s), s = v/(2+v), with atanh(s)  */
+/* = s * sum_{j=0..8} s^(2j)/(2j+1) by Horner in s^2 with fma.               */
+/* ------------------------------------------------------------------------ */
+static float ln2_head(void) {
+  /* ln 2 rounded to fp32, with its 12 low significand bits cleared so that
+   * n*head is exact for |n| < 2^12. */
+  float l = (float)0.69314718055994530942;
+  uint32_t u;
+  memcpy(&u, &l, sizeof u);
+  u &= 0xFFFFF000u;
+  memcpy(&l, &u, sizeof l);
+  return l;
+}
+
+float oracle_exp_nonpos(float y) {
+  if (y < -87.0f) return 0.0f;
+  const float log2e = (float)1.44269504088896340736;
+  const float hi = ln2_head();
+  const float lo = (float)(0.69314718055994530942 - (double)hi);
+  float n = rintf(y * log2e);
+  float r = fmaf(-n, hi, y);
+  r = fmaf(-n, lo, r);
+  /* coefficients 1/i! rounded to fp32, i = 7 .. 0 */
+  static const double inv_fact[8] = {1.0, 1.0, 1.0 / 2, 1.0 / 6, 1.0 / 24, 1.0 / 120, 1.0 / 720, 1.0 / 5040};
+  float p = (float)inv_fact[7];
+  for (int i = 6; i >= 0; --i) p = fmaf(p, r, (float)inv_fact[i]);
+  return ldexpf(p, (int)n);
+}
+
+float oracle_log1p_unit(float v) {
+  float s = v / (2.0f + v);
+  float s2 = s * s;
+  float q = (float)(1.0 / 17.0);
+  for (int j = 7; j >= 0; --j) q = fmaf(q, s2, (float)(1.0 / (2 * j + 1)));
+  return (s + s) * q;
+}
+
+float oracle_softplus(float z) {
+  if (z > 20.0f) return z;
+  float v = oracle_exp_nonpos(-fabsf(z));
+  float r = oracle_log1p_unit(v);
+  return z > 0.0f ? z + r : r;
+}
+
+void oracle_softplus_n(const float* z, float* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_softplus(z[i]);
+}
+
+void oracle_exp_nonpos_n(const float* y, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_exp_nonpos(y[i]);
+}
+
+void oracle_log1p_unit_n(const float* v, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_log1p_unit(v[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gate logits.                                                              */
+/* [Shazeer] "Noisy Top-K Gating": H(x)_i = (x W_g)_i + N(0,1) *             */
+/* Softplus((x W_noise)_i); the plain gate is H = x W_g ([Switch] listing:   */
+/* a linear router layer). Canonical fp32 order (the reading that makes the  */
+/* top-k decision reproducible): each dot product starts at +0 and adds      */
+/* x[j]*W[j][e] for j = 0, 1, ..., d-1 with one fused multiply-add per term. */
+/* An optional per-expert bias b[e] (used to skew routing) is added after    */
+/* the sum with one rounding; the noise term is fma(eps, softplus, clean).   */
+/* Outputs, all [T,E] fp32: clean logits, noise scale sigma (noisy only) and */
+/* H. sigma and w_noise/noise may be NULL for the plain gate (then H=clean). */
+/* ------------------------------------------------------------------------ */
+/* Hot loops are built twice (baseline x86-64 and Haswell FMA/AVX2) and the
+ * loader picks one by CPU; fmaf rounds once either way. */
+#define ORACLE_HOT __attribute__((target_clones("default", "arch=haswell")))
+
+ORACLE_HOT void oracle_gate_logits(int64_t T, int d, int E, int dtype, const void* x, const void* w_gate,
+                        const float* gate_bias, const void* w_noise, const float* noise,
+                        float* clean, float* sigma, float* H) {
+  float* wg = (float*)malloc(sizeof(float) * (size_t)d * (size_t)E);
+  float* wn = w_noise ? (float*)malloc(sizeof(float) * (size_t)d * (size_t)E) : NULL;
+  for (int64_t i = 0; i < (int64_t)d * E; ++i) {
+    wg[i] = elem(w_gate, dtype, i);
+    if (wn) wn[i] = elem(w_noise, dtype, i);
+  }
+#pragma omp parallel
+  {
+    float* xr = (float*)malloc(sizeof(float) * (size_t)d);
+    float* acc = (float*)malloc(sizeof(float) * (size_t)E);
+    float* accn = (float*)malloc(sizeof(float) * (size_t)E);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      for (int j = 0; j < d; ++j) xr[j] = elem(x, dtype, t * d + j);
+      for (int e = 0; e < E; ++e) acc[e] = accn[e] = 0.0f;
+      for (int j = 0; j < d; ++j) {
+        const float xj = xr[j];
+        const float* wrow = wg + (size_t)j * E;
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(xj, wrow[e], acc[e]);
+        if (wn) {
+          const float* nrow = wn + (size_t)j * E;
+          for (int e = 0; e < E; ++e) accn[e] = fmaf(xj, nrow[e], accn[e]);
+        }
+      }
+      for (int e = 0; e < E; ++e) {
+        float c = gate_bias ? acc[e] + gate_bias[e] : acc[e];
+        clean[t * E + e] = c;
+        if (wn) {
+          float sg = oracle_softplus(accn[e]);
+          if (sigma) sigma[t * E + e] = sg;
+          H[t * E + e] = fmaf(noise[t * E + e], sg, c);
+        } else {
+          H[t * E + e] = c;
+        }
+      }
+    }
+    free(xr);
+    free(acc);
+    free(accn);
+  }
+  free(wg);
+  free(wn);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Top-k order.                                                              */
+/* [Shazeer] KeepTopK keeps the k largest entries of H; [Switch] top-1 on    */
+/* the softmax, which orders experts exactly as H does. Ties are not         */
+/* treated on the pages; reading: the lower expert index wins (-0 == +0).    */
+/* Writes the first kk experts of the order (H descending, index ascending). */
+/* Precondition: H finite.                                                   */
+/* ------------------------------------------------------------------------ */
+void oracle_topk_order(int64_t T, int E, int kk, const float* H, int32_t* order) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    const float* h = H + t * E;
+    for (int s = 0; s < kk; ++s) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        int taken = 0;
+        for (int q = 0; q < s; ++q)
+          if (order[t * kk + q] == e) taken = 1;
+        if (taken) continue;
+        if (best < 0 || h[e] > h[best]) best = e; /* strict '>' keeps the lower index on ties */
+      }
+      order[t * kk + s] = best;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gate values, fp64.                                                        */
+/* renormalize = 1: [Shazeer] G = Softmax(KeepTopK(H, k)) -- the softmax     */
+/*   over the k kept logits, g_s = exp(H_s - H_0) / sum_s' exp(H_s' - H_0).  */
+/* renormalize = 0: [Switch] listing, gate = mask * softmax(logits): the raw */
+/*   full-softmax probability of each kept expert.                           */
+/* prob (optional, [T,E]): the full softmax over all E experts.              */
+/* ------------------------------------------------------------------------ */
+void oracle_gates(int64_t T, int E, int k, int renormalize, const float* H, const int32_t* topk_idx,
+                  double* gates, double* prob) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    const float* h = H + t * E;
+    double m = -INFINITY;
+    for (int e = 0; e < E; ++e)
+      if ((double)h[e] > m) m = h[e];
+    double z = 0.0;
+    for (int e = 0; e < E; ++e) z += exp((double)h[e] - m);
+    if (prob)
+      for (int e = 0; e < E; ++e) prob[t * E + e] = exp((double)h[e] - m) / z;
+    const int32_t* idx = topk_idx + t * k;
+    if (renormalize) {
+      double h0 = h[idx[0]];
+      double zk = 0.0;
+      for (int s = 0; s < k; ++s) zk += exp((double)h[idx[s]] - h0);
+      for (int s = 0; s < k; ++s) gates[t * k + s] = exp((double)h[idx[s]] - h0) / zk;
+    } else {
+      for (int s = 0; s < k; ++s) gates[t * k + s] = exp((double)h[idx[s]] - m) / z;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Smooth load estimator, fp64 ([Shazeer] "Load-Balancing-Losses"):          */
+/*   P(x,i) = Phi((clean_i - kth_excluding(H, k, i)) / sigma_i),             */
+/* where clean is the noise-free logit (x W_g, plus bias if any) and         */
+/* kth_excluding(H, k, i) is the k-th largest H_j over j != i. That is the   */
+/* (k+1)-th largest overall when i is in the top k, else the k-th largest.   */
+/* With k == E there is no (k+1)-th value and P = 1 for every expert.        */
+/* order: [T, kk] with kk = min(k+1, E). Writes load[E] = sum_x P(x, i).     */
+/* ------------------------------------------------------------------------ */
+static double std_normal_cdf(double z) { return 0.5 * erfc(-z / sqrt(2.0)); }
+
+void oracle_load(int64_t T, int E, int k, const float* clean, const float* sigma, const float* H,
+                 const int32_t* order, int kk, double* load) {
+  for (int e = 0; e < E; ++e) load[e] = 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    const int32_t* o = order + t * kk;
+    double thr_out = H[t * E + o[k - 1]];
+    int have_in = kk > k;
+    double thr_in = have_in ? (double)H[t * E + o[k]] : -INFINITY;
+    for (int e = 0; e < E; ++e) {
+      int in_topk = 0;
+      for (int s = 0; s < k; ++s)
+        if (o[s] == e) in_topk = 1;
+      double p;
+      if (in_topk && !have_in) {
+        p = 1.0;
+      } else {
+        double thr = in_topk ? thr_in : thr_out;
+        p = std_normal_cdf(((double)clean[t * E + e] - thr) / (double)sigma[t * E + e]);
+      }
+      load[e] += p;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Balancing losses (unweighted; the caller applies its weights).            */
+/* [Shazeer] "Load-Balancing-Losses": Importance(X) = sum over the batch of  */
+/*   G(x); L = w * CV(.)^2. CV is read as population std / mean; CV^2 = 0    */
+/*   for E = 1.                                                              */
+/* [Switch] names an auxiliary load-balancing loss without a formula; the    */
+/*   reading is the Switch Transformer paper's E * sum_e f_e * P_e with f_e  */
+/*   the fraction of the T*k assignments routed to e (before capacity drops) */
+/*   and P_e the batch mean of the full-softmax probability of e.            */
+/* aux[0] = switch loss, aux[1] = CV^2(importance), aux[2] = CV^2(load) or   */
+/* NaN when load is NULL.                                                    */
+/* ------------------------------------------------------------------------ */
+static double cv_squared(const double* v, int E) {
+  if (E <= 1) return 0.0;
+  double mean = 0.0;
+  for (int e = 0; e < E; ++e) mean += v[e];
+  mean /= E;
+  double var = 0.0;
+  for (int e = 0; e < E; ++e) var += (v[e] - mean) * (v[e] - mean);
+  var /= E;
+  return var / (mean * mean);
+}
+
+void oracle_aux(int64_t T, int E, int k, const int32_t* counts_routed, const double* prob_sum,
+                const double* importance, const double* load, double* aux) {
+  double s = 0.0;
+  for (int e = 0; e < E; ++e) {
+    double f = (double)counts_routed[e] / ((double)T * (double)k);
+    double P = prob_sum[e] / (double)T;
+    s += f * P;
+  }
+  aux[0] = (double)E * s;
+  aux[1] = cv_squared(importance, E);
+  aux[2] = load ? cv_squared(load, E) : NAN;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Capacity. [Tables] give capacity factors only, no formula. Reading:       */
+/* C = ceil(cf * k * T / E) evaluated in double; cf <= 0 means no limit; an  */
+/* explicit capacity >= 0 overrides the factor. Returns -1 for no limit.     */
+/* ------------------------------------------------------------------------ */
+int64_t oracle_capacity(int64_t T, int E, int k, double capacity_factor, int64_t capacity) {
+  if (capacity >= 0) return capacity;
+  if (!(capacity_factor > 0.0)) return -1;
+  return (int64_t)ceil(capacity_factor * (double)k * (double)T / (double)E);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dispatch: group the T*k assignments by expert ([Switch] listing, per      */
+/* expert gather; [Shazeer] "Methode": computation is skipped where the gate */
+/* is zero). Walk tokens in order and, inside a token, its slots in order;   */
+/* each assignment takes the next rank of its expert; ranks >= C are        */
+/* dropped (overflow dropped in token order). counts_kept = min(routed, C);  */
+/* offsets = exclusive prefix sum of counts_kept over experts (E+1 entries); */
+/* slot_dest[t,s] = offsets[e] + rank for kept assignments, else -1;         */
+/* row_src[slot] = t. Rows of the permuted batch are therefore sorted by     */
+/* (expert, token). C < 0 means no limit.                                    */
+/* ------------------------------------------------------------------------ */
+void oracle_dispatch(int64_t T, int E, int k, int64_t C, const int32_t* topk_idx, int32_t* counts_routed,
+                     int32_t* counts_kept, int32_t* offsets, int32_t* slot_dest, int32_t* row_src) {
+  int64_t* fill = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+  int64_t* rank = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T * k > 0 ? T * k : 1));
+  for (int64_t t = 0; t < T; ++t)
+    for (int s = 0; s < k; ++s) {
+      int e = topk_idx[t * k + s];
+      rank[t * k + s] = fill[e]++;
+    }
+  int64_t acc = 0;
+  for (int e = 0; e < E; ++e) {
+    counts_routed[e] = (int32_t)fill[e];
+    int64_t kept = (C >= 0 && fill[e] > C) ? C : fill[e];
+    counts_kept[e] = (int32_t)kept;
+    offsets[e] = (int32_t)acc;
+    acc += kept;
+  }
+  offsets[E] = (int32_t)acc;
+  for (int64_t t = 0; t < T; ++t)
+    for (int s = 0; s < k; ++s) {
+      int e = topk_idx[t * k + s];
+      int64_t r = rank[t * k + s];
+      if (C >= 0 && r >= C) {
+        slot_dest[t * k + s] = -1;
+      } else {
+        int64_t slot = offsets[e] + r;
+        slot_dest[t * k + s] = (int32_t)slot;
+        row_src[slot] = (int32_t)t;
+      }
+    }
+  free(fill);
+  free(rank);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert feed-forward network, fp64 ([Shazeer] abstract and "Methode":      */
+/* experts are feed-forward sub-networks). Reading: two layers without       */
+/* biases, y = act(x W1[e]) W2[e], act = ReLU or the exact GELU              */
+/* 0.5 z (1 + erf(z / sqrt 2)). Evaluates n rows: row r applies expert       */
+/* expert[r] to row x_row[r] of x [*, d]. out: [n, d] fp64.                  */
+/* ------------------------------------------------------------------------ */
+ORACLE_HOT void oracle_expert_ffn_rows(int64_t n, int d, int f, int dtype, int act, const void* x, const int32_t* x_row,
+                            const int32_t* expert, const void* w1, const void* w2, double* out) {
+#pragma omp parallel
+  {
+    double* h = (double*)malloc(sizeof(double) * (size_t)f);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+      const int64_t t = x_row[r];
+      const int64_t e = expert[r];
+      for (int i = 0; i < f; ++i) h[i] = 0.0;
+      for (int j = 0; j < d; ++j) {
+        const double xj = elem(x, dtype, t * d + j);
+        const int64_t base = (e * d + j) * (int64_t)f;
+        for (int i = 0; i < f; ++i) h[i] += xj * (double)elem(w1, dtype, base + i);
+      }
+      for (int i = 0; i < f; ++i) {
+        double z = h[i];
+        h[i] = (act == OR_RELU) ? (z > 0.0 ? z : 0.0) : 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
+      }
+      double* o = out + r * d;
+      for (int j = 0; j < d; ++j) o[j] = 0.0;
+      for (int i = 0; i < f; ++i) {
+        const double hi = h[i];
+        const int64_t base = (e * f + i) * (int64_t)d;
+        for (int j = 0; j < d; ++j) o[j] += hi * (double)elem(w2, dtype, base + j);
+      }
+    }
+    free(h);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Combine ([Shazeer] "Methode": y = sum_i G(x)_i E_i(x); [Switch] listing:  */
+/* the per-expert outputs are added back at their tokens). For each token t */
+/* in tokens[], y[t] = sum over kept slots s (slot order) of                 */
+/* gate[t,s] * Yp[slot_dest[t,s]]. A dropped slot contributes nothing and    */
+/* surviving gates are not rescaled; a token with every slot dropped gets a  */
+/* zero row. yp_row_of_slot maps a slot index to a row of yp (identity when  */
+/* NULL), so a caller can pass only the rows it evaluated.                   */
+/* ------------------------------------------------------------------------ */
+void oracle_combine(int64_t n_tokens, const int32_t* tokens, int d, int k, const int32_t* slot_dest,
+                    const double* gates, const double* yp, const int32_t* yp_row_of_slot, double* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n_tokens; ++i) {
+    const int64_t t = tokens[i];
+    double* o = y + i * d;
+    for (int j = 0; j < d; ++j) o[j] = 0.0;
+    for (int s = 0; s < k; ++s) {
+      const int32_t slot = slot_dest[t * k + s];
+      if (slot < 0) continue;
+      const int64_t row = yp_row_of_slot ? yp_row_of_slot[slot] : slot;
+      const double g = gates[t * k + s];
+      for (int j = 0; j < d; ++j) o[j] += g * yp[row * d + j];
+    }
+  }
+}
