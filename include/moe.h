@@ -1,0 +1,196 @@
+/*
+ * moe.h -- C ABI of the gfx950 (MI355X) forward pass of one sparsely-gated
+ * Mixture-of-Experts layer.
+ *
+ * The layer, from the pages:
+ *   - Shazeer et al. summary page ("Outrageously Large Neural Networks: The
+ *     Sparsely-Gated Mixture-of-Experts Layer"), section "Methode": the layer
+ *     output y = sum_i G(x)_i E_i(x), skipping experts whose gate is zero;
+ *     noisy top-k gating H(x)_i = (x W_g)_i + StandardNormal() *
+ *     Softplus((x W_noise)_i), G(x) = Softmax(KeepTopK(H(x), k)); and the
+ *     importance / load balancing losses, CV(.)^2 of per-expert sums.
+ *   - "Switch Transformer" page: top-1 routing; its listing takes the softmax
+ *     over all experts, keeps the top-1 probability as the gate and gathers
+ *     each expert's tokens; an auxiliary load-balancing loss is named.
+ *   - "moe paper models" page, table 2: capacity factors (1.25, 1/1.5/2x, 2).
+ *
+ * Conventions (all entry points):
+ *   - Every pointer argument is a DEVICE pointer to contiguous row-major data,
+ *     aligned to 16 bytes, owned by the caller, unless stated otherwise. The
+ *     library allocates no device memory and keeps no state between calls
+ *     except a thread-local error string.
+ *   - "dtype" tensors (x, w_gate, w_noise, w1, w2, x_perm, y_perm, y) are all
+ *     bf16 (raw 16-bit patterns) or all fp32, per moe_params.dtype. Logits,
+ *     gates, noise, gate_bias and aux are always fp32; indices are int32.
+ *   - Calls enqueue kernels on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return without synchronising. Outputs are valid once the
+ *     stream reaches them.
+ *   - Errors: arguments are checked before anything is enqueued; a failing
+ *     check returns MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED or
+ *     MOE_ERR_WORKSPACE, enqueues nothing, and sets moe_last_error(). A failed
+ *     launch returns MOE_ERR_HIP. Faults inside kernels surface at the
+ *     caller's next synchronisation. Capacity overflow is not an error: the
+ *     overflowing assignments are dropped.
+ *   - Preconditions not checked on the device: inputs finite (no NaN/Inf);
+ *     pointers valid for the documented extents.
+ *   - Supported domain: T >= 0, T*k < 2^31, 1 <= E <= 1024, 1 <= k <= min(E, 8),
+ *     d_model and d_ff positive multiples of 8.
+ *   - Workspace: `ws` is caller-owned device scratch of at least
+ *     moe_workspace_size() bytes for that entry point, 256-byte aligned. Two
+ *     calls that may run at the same time need separate workspaces.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a pointer, size or option outside the documented domain */
+  MOE_ERR_UNSUPPORTED = 2, /* outside the supported domain (e.g. d_model % 8 != 0, E > 1024) */
+  MOE_ERR_WORKSPACE = 3,   /* ws NULL, misaligned or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+enum { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1 }; /* GELU is the exact 0.5 z (1 + erf(z / sqrt 2)) */
+enum { MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2, MOE_OP_FORWARD = 3 };
+
+typedef struct moe_params {
+  int64_t T;               /* tokens in the batch */
+  int32_t d_model;         /* token width d */
+  int32_t d_ff;            /* expert hidden width f */
+  int32_t E;               /* number of experts */
+  int32_t k;               /* experts per token */
+  int32_t dtype;           /* MOE_F32 or MOE_BF16 */
+  int32_t act;             /* MOE_ACT_RELU or MOE_ACT_GELU */
+  int32_t renormalize;     /* 1: gates = softmax over the k kept logits (Shazeer, KeepTopK + Softmax);
+                              0: gates = full-softmax probabilities of the kept experts (Switch listing) */
+  int32_t reserved;        /* must be 0 */
+  double capacity_factor;  /* > 0: per-expert capacity C = ceil(capacity_factor * k * T / E); <= 0: none */
+  int64_t capacity;        /* >= 0: explicit per-expert capacity C (overrides capacity_factor); < 0: unused */
+} moe_params;
+
+/* Human-readable name of a status code. Never NULL; static storage. */
+const char* moe_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Per-expert capacity C for p (see moe_params), -1 if unlimited, -2 if p is
+ * invalid. Host-only; no HIP call. */
+int64_t moe_capacity(const moe_params* p);
+
+/* Upper bound on kept rows R = sum_e min(routed_e, C): min(T*k, E*C). Sizes
+ * x_perm / y_perm / row_src. Host-only. Returns -1 if p is invalid. */
+int64_t moe_max_rows(const moe_params* p);
+
+/* Workspace bytes needed by entry point `op` (MOE_OP_*) for p. Host-only. */
+moe_status moe_workspace_size(const moe_params* p, int op, size_t* bytes);
+
+/*
+ * moe_route -- gate logits, top-k, gate values, routed counts, balancing losses.
+ *   (Shazeer "Methode": Noisy Top-K Gating and Load-Balancing-Losses;
+ *    Switch page: softmax over all experts and top-1.)
+ * Logits, in fp32 with a fixed order of operations (the order is part of the
+ * contract; it makes the integer routing reproducible bit-for-bit):
+ *   clean[t,e] = (sum_{j=0..d-1, ascending} fma-accumulated x[t,j]*w_gate[j,e]) (+ gate_bias[e])
+ *   H[t,e]     = fma(noise[t,e], softplus(x[t,:] . w_noise[:,e]), clean[t,e])   if w_noise
+ *              = clean[t,e]                                                    otherwise
+ * with the dot products accumulated from +0 in ascending j, one fma per term,
+ * and softplus built from IEEE fp32 basic operations (exp by Cody-Waite
+ * reduction + degree-7 Taylor/Horner, log1p via 2*atanh(v/(2+v)) with a
+ * degree-8 odd series; z > 20 returns z; exp is 0 below -87).
+ * Experts are ordered by H descending, ties to the lower index; slot s < k
+ * takes the s-th. Gates (fp32): renormalize=1: softmax over the kept logits;
+ * 0: full-softmax probability.
+ * Inputs:  x [T,d] dtype; w_gate [d,E] dtype; gate_bias [E] fp32 or NULL;
+ *          w_noise [d,E] dtype or NULL; noise [T,E] fp32 standard normals
+ *          (required iff w_noise).
+ * Outputs: topk_idx [T,k] int32; topk_gate [T,k] fp32;
+ *          counts_routed [E] int32 (assignments per expert, before capacity);
+ *          aux_out [3] fp32 or NULL: {E*sum_e f_e*P_e with f_e = routed_e/(T*k) and
+ *            P_e = mean_t softmax(H_t)_e; CV^2 of importance_e = sum of the gates
+ *            routed to e; CV^2 of load_e = sum_t Phi((clean[t,e] - kth_excluding(H_t,k,e))
+ *            / softplus(...)) -- NaN without w_noise}; CV^2 uses the population variance;
+ *          logits_out [T,E] fp32 (H) or NULL.
+ */
+moe_status moe_route(const moe_params* p, const void* x, const void* w_gate, const float* gate_bias,
+                     const void* w_noise, const float* noise, int32_t* topk_idx, float* topk_gate,
+                     int32_t* counts_routed, float* aux_out, float* logits_out, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * moe_dispatch -- group assignments by expert with capacity drops in token order.
+ *   (Switch listing: per-expert gather of the routed tokens; "moe paper
+ *    models" table 2: capacity factors.)
+ * The T*k assignments are walked in token order (slot order within a token);
+ * each takes the next rank of its expert; rank >= C is dropped.
+ * Inputs:  x [T,d] dtype; topk_idx [T,k] int32 (values in [0,E), distinct per token).
+ * Outputs: counts_kept [E] int32 = min(routed_e, C);
+ *          offsets [E+1] int32, exclusive prefix sum of counts_kept (offsets[E] = R);
+ *          slot_dest [T,k] int32: row of the assignment in x_perm, or -1 if dropped;
+ *          row_src [moe_max_rows] int32: token of each row (entries >= R untouched);
+ *          x_perm [moe_max_rows, d] dtype: x_perm[r] = x[row_src[r]] (rows >= R untouched).
+ * Rows are sorted by (expert, token).
+ */
+moe_status moe_dispatch(const moe_params* p, const void* x, const int32_t* topk_idx, int32_t* counts_kept,
+                        int32_t* offsets, int32_t* slot_dest, int32_t* row_src, void* x_perm, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- every expert's two-layer FFN on its contiguous row segment.
+ *   (Shazeer abstract / "Methode": experts are feed-forward sub-networks.)
+ *   y_perm[r] = act(x_perm[r] . w1[e]) . w2[e] for offsets[e] <= r < offsets[e+1],
+ * no biases; products accumulate in fp32; for bf16 the hidden activation is
+ * rounded to bf16 (nearest-even) before the second product.
+ * Inputs:  x_perm [R,d] dtype; offsets [E+1] int32 (device; R = offsets[E] <= moe_max_rows);
+ *          w1 [E,d,f] dtype; w2 [E,f,d] dtype.
+ * Outputs: y_perm [R,d] dtype (rows >= R untouched).
+ */
+moe_status moe_expert_ffn(const moe_params* p, const void* x_perm, const int32_t* offsets, const void* w1,
+                          const void* w2, void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- gate-weighted sum back into token order.
+ *   (Shazeer "Methode": y = sum_i G(x)_i E_i(x); Switch listing: expert outputs
+ *    added back at their tokens.)
+ *   y[t] = sum over s = 0..k-1 with slot_dest[t,s] >= 0 of topk_gate[t,s] * y_perm[slot_dest[t,s]],
+ * accumulated in fp32 in slot order; a token with every slot dropped gets 0.
+ * Dropped gates are not redistributed.
+ * Inputs:  y_perm [R,d] dtype; slot_dest [T,k] int32; topk_gate [T,k] fp32.
+ * Outputs: y [T,d] dtype.
+ */
+moe_status moe_combine(const moe_params* p, const void* y_perm, const int32_t* slot_dest, const float* topk_gate,
+                       void* y, void* stream);
+
+/*
+ * moe_forward -- the whole layer: moe_route, moe_dispatch, moe_expert_ffn and
+ * moe_combine on one stream, intermediates in `ws`.
+ * Inputs as moe_route plus w1, w2. Outputs: y [T,d] dtype (required);
+ * aux_out [3], topk_idx [T,k], topk_gate [T,k], counts_routed [E], counts_kept [E],
+ * slot_dest [T,k] -- each optional (NULL: kept in the workspace only).
+ */
+moe_status moe_forward(const moe_params* p, const void* x, const void* w_gate, const float* gate_bias,
+                       const void* w_noise, const float* noise, const void* w1, const void* w2, void* y,
+                       float* aux_out, int32_t* topk_idx, float* topk_gate, int32_t* counts_routed,
+                       int32_t* counts_kept, int32_t* slot_dest, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_canonical_softplus -- the softplus of the noisy gate (Shazeer "Methode",
+ * Noisy Top-K Gating: Softplus((x W_noise)_i)), element-wise, exactly as
+ * moe_route evaluates it (see the definition above moe_route).
+ * Inputs: z [n] fp32. Outputs: out [n] fp32. n >= 0.
+ */
+moe_status moe_canonical_softplus(const float* z, float* out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,101 @@
+// common.h -- device helpers and launch declarations shared by the gfx950
+// kernels of the MoE layer forward. Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// bf16 values travel as raw 16-bit patterns (uint16_t); widening is exact.
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Activation of the first expert layer: ReLU, or the exact GELU 0.5 z (1 + erf(z / sqrt 2)).
+template <int ACT>
+__device__ __forceinline__ float activation(float z) {
+  if constexpr (ACT == 0) {
+    return z > 0.0f ? z : 0.0f;
+  } else {
+    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+  }
+}
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// Launchers (host). Each returns the hipError_t of its launches.
+// ---------------------------------------------------------------------------
+struct RouteLaunch {
+  int64_t T;
+  int d, E, k, dtype, renormalize;
+  const void* x;
+  const void* w_gate;
+  const float* gate_bias;
+  const void* w_noise;
+  const float* noise;
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t* counts_routed;
+  float* aux_out;
+  float* logits_out;
+  // workspace pieces
+  float* part_prob;  // [E][nblk]
+  float* part_imp;   // [E][nblk]
+  float* part_load;  // [E][nblk]
+  int32_t* part_cnt; // [E][nblk]
+  double* red;       // [3][E]
+};
+int route_tokens_per_block(int E, bool noisy);
+hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
+
+struct DispatchLaunch {
+  int64_t T;
+  int d, E, k, dtype;
+  int64_t C;  // < 0: unlimited
+  int64_t max_rows;
+  const void* x;
+  const int32_t* topk_idx;
+  int32_t* counts_kept;
+  int32_t* offsets;
+  int32_t* slot_dest;
+  int32_t* row_src;
+  void* x_perm;
+  int32_t* blk_cnt;  // [E][nb] workspace
+};
+int64_t dispatch_num_blocks(int64_t assignments);
+hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s);
+
+struct FfnLaunch {
+  int d, f, E, dtype, act;
+  int64_t max_rows;
+  const void* x_perm;
+  const int32_t* offsets;
+  const void* w1;
+  const void* w2;
+  void* y_perm;
+  void* h1;             // [max_rows, f] dtype workspace
+  int32_t* tile_start;  // [E+1] workspace
+};
+hipError_t launch_expert_ffn(const FfnLaunch& a, hipStream_t s);
+
+struct CombineLaunch {
+  int64_t T;
+  int d, k, dtype;
+  const void* y_perm;
+  const int32_t* slot_dest;
+  const float* topk_gate;
+  void* y;
+};
+hipError_t launch_combine(const CombineLaunch& a, hipStream_t s);

@@ -1,0 +1,166 @@
+// dispatch.hip -- group the T*k assignments by expert, keep the first C of
+// each expert in token order, and copy the kept token rows into one
+// expert-sorted buffer.
+//
+// Method: the "Switch Transformer" page's listing gathers, for each expert,
+// the tokens routed to it; the "moe paper models" table 2 lists capacity
+// factors (a per-expert buffer size). Overflow is dropped in token order:
+// walking tokens in order (slots in order within a token), each assignment
+// takes the next rank of its expert and is kept iff rank < C.
+//
+// Design (gfx950), four launches, all integer work exact and deterministic:
+//   count   per 1024-assignment block, per-expert counts (LDS integer atomics);
+//   scan    one block: for each expert, exclusive prefix over blocks (the
+//           block's base rank), kept = min(count, C), offsets = exclusive
+//           prefix over experts;
+//   rank    per block: stable ranks inside each wave from 64-lane ballots on
+//           the bits of the expert id (multisplit), per-wave running counts in
+//           LDS, then base + earlier waves + in-wave rank -> slot or -1;
+//   permute one 16-byte chunk per thread: x_perm[r] = x[row_src[r]], reads of
+//           whole rows, fully coalesced writes.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = 1024;  // assignments per block: 4 waves x 4 steps x 64 lanes
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx, int64_t n, int E,
+                                                             int nb, int32_t* __restrict__ blk_cnt) {
+  extern __shared__ int hist[];
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kChunk;
+  for (int i = threadIdx.x; i < kChunk; i += 256) {
+    const int64_t a = base + i;
+    if (a < n) atomicAdd(&hist[idx[a]], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) blk_cnt[(int64_t)e * nb + blockIdx.x] = hist[e];
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ blk_cnt, int nb, int E,
+                                                             int64_t C, int32_t* __restrict__ counts_kept,
+                                                             int32_t* __restrict__ offsets) {
+  __shared__ int64_t sc[1024];
+  const int e = threadIdx.x;
+  int64_t run = 0;
+  if (e < E) {
+    int32_t* row = blk_cnt + (int64_t)e * nb;
+    for (int b = 0; b < nb; ++b) {
+      const int32_t c = row[b];
+      row[b] = (int32_t)run;
+      run += c;
+    }
+  }
+  const int64_t kept = (e < E) ? ((C >= 0 && run > C) ? C : run) : 0;
+  if (e < E) counts_kept[e] = (int32_t)kept;
+  sc[e] = kept;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int64_t v = e >= off ? sc[e - off] : 0;
+    __syncthreads();
+    sc[e] += v;
+    __syncthreads();
+  }
+  if (e < E) offsets[e] = (int32_t)(sc[e] - kept);
+  if (e == E - 1) offsets[E] = (int32_t)sc[e];
+}
+
+__global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __restrict__ idx, int64_t n, int k,
+                                                            int E, int nbits, int nb, int64_t C,
+                                                            const int32_t* __restrict__ blk_base,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ slot_dest,
+                                                            int32_t* __restrict__ row_src) {
+  extern __shared__ int wcnt[];  // [4 waves][E] running counts
+  for (int i = threadIdx.x; i < 4 * E; i += 256) wcnt[i] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t base = (int64_t)blockIdx.x * kChunk + wave * 256;
+  int ex[4], loc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t a = base + q * 64 + lane;
+    const bool valid = a < n;
+    const int e = valid ? idx[a] : 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = __ballot(valid && bit);
+      same &= bit ? ones : ~ones;
+    }
+    const int before_in_wave = __popcll(same & lt_mask);
+    const int prev = valid ? wcnt[wave * E + e] : 0;
+    loc[q] = prev + before_in_wave;
+    ex[q] = valid ? e : -1;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && before_in_wave == 0) wcnt[wave * E + e] = prev + __popcll(same);
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = ex[q];
+    if (e < 0) continue;
+    const int64_t a = base + q * 64 + lane;
+    int64_t r = (int64_t)blk_base[(int64_t)e * nb + blockIdx.x] + loc[q];
+    for (int w = 0; w < wave; ++w) r += wcnt[w * E + e];
+    const bool keep = C < 0 || r < C;
+    const int32_t slot = keep ? (int32_t)(offsets[e] + r) : -1;
+    slot_dest[a] = slot;
+    if (keep) row_src[slot] = (int32_t)(a / k);
+  }
+}
+
+// x_perm[r, :] = x[row_src[r], :] for r < offsets[E]; 16-byte chunks.
+__global__ __launch_bounds__(256) void permute_rows_kernel(const uint4* __restrict__ x,
+                                                           const int32_t* __restrict__ row_src,
+                                                           const int32_t* __restrict__ offsets, int E,
+                                                           int chunks_per_row, int64_t total,
+                                                           uint4* __restrict__ xp) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t r = i / chunks_per_row;
+  if (r >= offsets[E]) return;
+  const int64_t c = i - r * chunks_per_row;
+  xp[i] = x[(int64_t)row_src[r] * chunks_per_row + c];
+}
+
+}  // namespace
+}  // namespace moe
+
+int64_t dispatch_num_blocks(int64_t assignments) { return (assignments + moe::kChunk - 1) / moe::kChunk; }
+
+hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s) {
+  using namespace moe;
+  const int64_t n = a.T * a.k;
+  const int nb = (int)dispatch_num_blocks(n);
+  hipError_t err;
+  if (nb > 0) {
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nb), dim3(256), sizeof(int) * a.E, s, a.topk_idx, n, a.E, nb,
+                       a.blk_cnt);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, a.blk_cnt, nb, a.E, a.C, a.counts_kept,
+                     a.offsets);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (nb == 0) return hipSuccess;
+  int nbits = 0;
+  while ((1 << nbits) < a.E) ++nbits;
+  hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nb), dim3(256), sizeof(int) * 4 * a.E, s, a.topk_idx, n, a.k, a.E,
+                     nbits, nb, a.C, a.blk_cnt, a.offsets, a.slot_dest, a.row_src);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int elt = a.dtype == 1 ? 2 : 4;
+  const int cpr = a.d * elt / 16;
+  const int64_t total = a.max_rows * cpr;
+  if (total > 0) {
+    hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint4*>(a.x), a.row_src, a.offsets, a.E, cpr, total,
+                       static_cast<uint4*>(a.x_perm));
+    err = hipGetLastError();
+  }
+  return err;
+}

@@ -2,16 +2,19 @@
 
 Recipe: ``numpy.random.Generator(PCG64(s))`` for ``s`` in
 ``SeedSequence(seed).spawn(6)``, one stream per tensor in the fixed order
-x, W_gate, W_noise, noise, W1, W2. Each tensor is drawn as float32 standard
+x, W_gate, W_noise, noise, W1, W2. W1 and W2 use one child stream per expert
+(``s.spawn(E)``), so experts are drawn in parallel threads with a result that
+does not depend on the thread count. Each tensor is drawn as float32 standard
 normals, scaled by its standard deviation, and, for bf16 workloads, rounded to
-bf16 with round-to-nearest-even. W1 and W2 are drawn one expert at a time so
-the float32 temporaries stay small. bf16 tensors are returned as ``uint16``
-bit patterns.
+bf16 with round-to-nearest-even. bf16 tensors are returned as ``uint16`` bit
+patterns.
 """
 
 from __future__ import annotations
 
+import concurrent.futures as cf
 import functools
+import os
 
 import numpy as np
 from scipy.special import log_ndtr
@@ -31,11 +34,38 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _normal(gen: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+def _normal(gen: np.random.Generator, shape, std: float, dtype: str, out=None) -> np.ndarray:
     a = gen.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
         a *= np.float32(std)
-    return f32_to_bf16_bits(a) if dtype == "bf16" else a
+    if dtype != "bf16":
+        if out is not None:
+            out[...] = a
+            return out
+        return a
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= np.uint32(16)
+    if out is not None:
+        out[...] = u
+        return out
+    return u.astype(np.uint16)
+
+
+def _expert_stack(seq: np.random.SeedSequence, E: int, shape, std: float, dtype: str) -> np.ndarray:
+    st = np.uint16 if dtype == "bf16" else np.float32
+    out = np.empty((E, *shape), dtype=st)
+    children = seq.spawn(E)
+
+    def one(e):
+        _normal(np.random.Generator(np.random.PCG64(children[e])), shape, std, dtype, out=out[e])
+
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, range(E)))
+    return out
 
 
 @functools.lru_cache(maxsize=8)
@@ -81,7 +111,7 @@ def make_inputs(cfg: MoEConfig, seed: int = 0, with_weights: bool = True) -> dic
     """
     T, d, f, E = cfg.T, cfg.d_model, cfg.d_ff, cfg.E
     ss = np.random.SeedSequence(seed).spawn(6)
-    g_x, g_wg, g_wn, g_eps, g_w1, g_w2 = (np.random.Generator(np.random.PCG64(s)) for s in ss)
+    g_x, g_wg, g_wn, g_eps = (np.random.Generator(np.random.PCG64(s)) for s in ss[:4])
     out: dict = {}
     out["x"] = _normal(g_x, (T, d), cfg.x_std, cfg.dtype)
     out["w_gate"] = _normal(g_wg, (d, E), cfg.wg_std, cfg.dtype)
@@ -101,13 +131,6 @@ def make_inputs(cfg: MoEConfig, seed: int = 0, with_weights: bool = True) -> dic
     else:
         out["gate_bias"] = None
     if with_weights:
-        st = np.uint16 if cfg.dtype == "bf16" else np.float32
-        w1 = np.empty((E, d, f), dtype=st)
-        w2 = np.empty((E, f, d), dtype=st)
-        for e in range(E):
-            w1[e] = _normal(g_w1, (d, f), cfg.w1_std, cfg.dtype)
-        for e in range(E):
-            w2[e] = _normal(g_w2, (f, d), cfg.w2_std, cfg.dtype)
-        out["w1"] = w1
-        out["w2"] = w2
+        out["w1"] = _expert_stack(ss[4], E, (d, f), cfg.w1_std, cfg.dtype)
+        out["w2"] = _expert_stack(ss[5], E, (f, d), cfg.w2_std, cfg.dtype)
     return out

@@ -18,3 +18,15 @@ def orc():
     import oracle
 
     return oracle
+
+
+@pytest.fixture(scope="session")
+def moelib():
+    """The built HIP library's Python binding (builds it first if it is missing)."""
+    from sparsely_gated_mixture_gate_amd import build as _b
+
+    if not os.path.exists(_b.LIB):
+        _b.build()
+    import sparsely_gated_mixture_gate_amd as m
+
+    return m

@@ -1,0 +1,303 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Full-size cases run the five layer workloads at their real shapes in the
+launch configuration the benchmark times; the oracle checks all integer
+outputs and the gate logits exactly, and the expert FFN / combine / layer
+output on sampled rows (segment edges + random rows) or sampled tokens.
+Small cases cover ragged and degenerate shapes element by element.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import GATE_ATOL, TOL, aux_ok, as_f64, rel_rows_ok, sample_rows, say
+from synthetic import CONFIGS, f32_to_bf16_bits, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["tiny_fp32", "switch_top1", "noisy_top4", "gshard_top2", "dropless_top1"]
+
+
+@pytest.fixture(scope="module")
+def dev(moelib):
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU (torch.cuda.is_available() is False)")
+    return torch.device("cuda:0")
+
+
+_CACHE: dict = {}
+
+
+def _case(name, **over):
+    """Seeded inputs, the oracle's routing + dispatch, and device copies (cached per case)."""
+    key = (name, tuple(sorted(over.items())))
+    if key in _CACHE:
+        return _CACHE[key]
+    from sparsely_gated_mixture_gate_amd.buffers import to_device
+
+    base = CONFIGS[name]
+    cap = over.pop("capacity", -1)
+    cfg = scaled(base, **over) if over else base
+    say(f"[case] generating {cfg.name}")
+    inp = make_inputs(cfg)
+    spec = oracle.LayerSpec.of(cfg, capacity=cap)
+    r = oracle.route(spec, inp)
+    C = oracle.capacity(cfg.T, cfg.E, cfg.k, cfg.capacity_factor, cap)
+    disp = oracle.dispatch(r["topk_idx"], cfg.E, C)
+    d_inp = {k_: to_device(v) for k_, v in inp.items()}
+    out = dict(cfg=cfg, spec=spec, inp=inp, route=r, C=C, disp=disp, dev=d_inp, cap=cap)
+    _CACHE[key] = out
+    return out
+
+
+def _params(moelib, c):
+    cfg = c["cfg"]
+    return moelib.make_params(cfg.T, cfg.d_model, cfg.d_ff, cfg.E, cfg.k, cfg.dtype, cfg.act, cfg.renormalize,
+                              cfg.capacity_factor, c["cap"])
+
+
+def test_canonical_softplus_bitwise(moelib, dev):
+    import torch
+
+    rng = np.random.default_rng(0)
+    lo, hi = np.float32(-100.0), np.float32(100.0)
+    # every 61st fp32 bit pattern in [-100, 100] plus random values and edges
+    pos = np.arange(0, int(np.array([hi]).view(np.uint32)[0]) + 1, 61, dtype=np.uint32).view(np.float32)
+    z = np.concatenate([pos, -pos, rng.uniform(lo, hi, 1 << 20).astype(np.float32),
+                        np.array([0.0, -0.0, 20.0, 20.000002, 19.999998, -87.0, -87.00001, 86.99999, -86.99999,
+                                  1e-30, -1e-30, 1e-45, -1e-45], np.float32)])
+    say(f"[softplus] n={z.size}")
+    zt = torch.from_numpy(z).to(dev)
+    out = torch.empty_like(zt)
+    moelib.moe_canonical_softplus(zt, out)
+    got = out.cpu().numpy()
+    ref = oracle.softplus(z)
+    bad = np.flatnonzero(got.view(np.uint32) != ref.view(np.uint32))
+    assert bad.size == 0, f"{bad.size} mismatches, e.g. z={z[bad[:5]]} gpu={got[bad[:5]]} cpu={ref[bad[:5]]}"
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_route_full_size(moelib, dev, name):
+    import torch
+    from sparsely_gated_mixture_gate_amd.buffers import StepBuffers, to_numpy
+
+    c = _case(name)
+    cfg, r, d = c["cfg"], c["route"], c["dev"]
+    p = _params(moelib, c)
+    b = StepBuffers.alloc(p, dev)
+    say(f"[route] {cfg.name}")
+    moelib.moe_route(p, d["x"], d["w_gate"], d["gate_bias"], d["w_noise"], d["noise"], b.topk_idx, b.topk_gate,
+                     b.counts_routed, b.aux, b.logits, b.ws_route)
+    torch.cuda.synchronize()
+    H = to_numpy(b.logits)
+    mism = np.flatnonzero(H.view(np.uint32).ravel() != r["H"].view(np.uint32).ravel())
+    assert mism.size == 0, f"{mism.size} logits differ bitwise (first flat index {mism[:3]})"
+    assert np.array_equal(to_numpy(b.topk_idx), r["topk_idx"])
+    assert np.array_equal(to_numpy(b.counts_routed), r["counts_routed"])
+    assert np.abs(to_numpy(b.topk_gate) - r["topk_gate"]).max() <= GATE_ATOL
+    aux_ok(to_numpy(b.aux), r["aux"], 1e-4)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_dispatch_full_size(moelib, dev, name):
+    import torch
+    from sparsely_gated_mixture_gate_amd.buffers import StepBuffers, to_device, to_numpy
+
+    c = _case(name)
+    cfg, disp, d = c["cfg"], c["disp"], c["dev"]
+    p = _params(moelib, c)
+    b = StepBuffers.alloc(p, dev)
+    idx = to_device(c["route"]["topk_idx"])
+    say(f"[dispatch] {cfg.name} R={disp['R']}")
+    moelib.moe_dispatch(p, d["x"], idx, b.counts_kept, b.offsets, b.slot_dest, b.row_src, b.x_perm, b.ws_dispatch)
+    torch.cuda.synchronize()
+    R = disp["R"]
+    assert np.array_equal(to_numpy(b.counts_kept), disp["counts_kept"])
+    assert np.array_equal(to_numpy(b.offsets), disp["offsets"])
+    assert np.array_equal(to_numpy(b.slot_dest), disp["slot_dest"])
+    assert np.array_equal(to_numpy(b.row_src)[:R], disp["row_src"])
+    xp = to_numpy(b.x_perm)[:R]
+    assert np.array_equal(xp, c["inp"]["x"][disp["row_src"]])  # bit-exact copy
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_expert_ffn_full_size(moelib, dev, name):
+    import torch
+    from sparsely_gated_mixture_gate_amd.buffers import StepBuffers, to_device, to_numpy
+
+    c = _case(name)
+    cfg, disp, d, inp = c["cfg"], c["disp"], c["dev"], c["inp"]
+    p = _params(moelib, c)
+    b = StepBuffers.alloc(p, dev)
+    R = disp["R"]
+    b.x_perm[:R] = to_device(inp["x"][disp["row_src"]])
+    offs = to_device(disp["offsets"])
+    say(f"[expert_ffn] {cfg.name} R={R}")
+    moelib.moe_expert_ffn(p, b.x_perm, offs, d["w1"], d["w2"], b.y_perm, b.ws_ffn)
+    torch.cuda.synchronize()
+    rows = np.arange(R) if R * cfg.d_model * cfg.d_ff <= 2**27 else sample_rows(disp["offsets"], 64)
+    row_exp = np.repeat(np.arange(cfg.E), disp["counts_kept"])
+    ref = oracle.expert_ffn_rows(inp["x"], disp["row_src"][rows], row_exp[rows], inp["w1"], inp["w2"], cfg.act,
+                                 cfg.dtype)
+    got = as_f64(to_numpy(b.y_perm)[rows], cfg.dtype)
+    rel_rows_ok(got, ref, TOL[cfg.dtype], f"y_perm {cfg.name}")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_combine_full_size(moelib, dev, name):
+    import torch
+    from sparsely_gated_mixture_gate_amd.buffers import StepBuffers, to_device, to_numpy
+
+    c = _case(name)
+    cfg, disp = c["cfg"], c["disp"]
+    p = _params(moelib, c)
+    b = StepBuffers.alloc(p, dev)
+    R = disp["R"]
+    rng = np.random.default_rng(1)
+    yp = rng.standard_normal((max(R, 1), cfg.d_model)).astype(np.float32)
+    if cfg.dtype == "bf16":
+        yp = f32_to_bf16_bits(yp)
+    gates32 = c["route"]["topk_gate"].astype(np.float32)
+    b.y_perm[: yp.shape[0]] = to_device(yp)
+    say(f"[combine] {cfg.name}")
+    moelib.moe_combine(p, b.y_perm, to_device(disp["slot_dest"]), to_device(gates32), b.y)
+    torch.cuda.synchronize()
+    ref = oracle.combine(np.arange(cfg.T), disp["slot_dest"], gates32.astype(np.float64), as_f64(yp, cfg.dtype))
+    rel_rows_ok(as_f64(to_numpy(b.y), cfg.dtype), ref, TOL[cfg.dtype], f"y {cfg.name}")
+
+
+def _run_forward(moelib, c, dev):
+    import torch
+    from sparsely_gated_mixture_gate_amd.buffers import ForwardBuffers
+
+    d = c["dev"]
+    p = _params(moelib, c)
+    fb = ForwardBuffers.alloc(p, dev)
+    moelib.moe_forward(p, d["x"], d["w_gate"], d["gate_bias"], d["w_noise"], d["noise"], d["w1"], d["w2"], fb.y,
+                       fb.aux, fb.topk_idx, fb.topk_gate, fb.counts_routed, fb.counts_kept, fb.slot_dest, fb.ws)
+    torch.cuda.synchronize()
+    return fb
+
+
+def _check_forward(c, fb, tokens):
+    from sparsely_gated_mixture_gate_amd.buffers import to_numpy
+
+    cfg, r, disp = c["cfg"], c["route"], c["disp"]
+    assert np.array_equal(to_numpy(fb.topk_idx), r["topk_idx"])
+    assert np.array_equal(to_numpy(fb.counts_routed), r["counts_routed"])
+    assert np.array_equal(to_numpy(fb.counts_kept), disp["counts_kept"])
+    assert np.array_equal(to_numpy(fb.slot_dest), disp["slot_dest"])
+    assert np.abs(to_numpy(fb.topk_gate) - r["topk_gate"]).max(initial=0.0) <= GATE_ATOL
+    aux_ok(to_numpy(fb.aux), r["aux"], 1e-4)
+    ref = oracle.forward(c["spec"], c["inp"], tokens=tokens)
+    got = as_f64(to_numpy(fb.y)[tokens], cfg.dtype)
+    rel_rows_ok(got, ref["y"], TOL[cfg.dtype], f"y {cfg.name}")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size(moelib, dev, name):
+    c = _case(name)
+    cfg = c["cfg"]
+    say(f"[forward] {cfg.name}")
+    fb = _run_forward(moelib, c, dev)
+    rng = np.random.default_rng(2)
+    n = cfg.T if cfg.T * cfg.d_model * cfg.d_ff <= 2**26 else 48
+    tokens = np.arange(cfg.T) if n == cfg.T else np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, n)]))
+    _check_forward(c, fb, tokens)
+
+
+SMALL = [
+    # (workload, overrides) -- ragged T, tiny and degenerate shapes
+    ("tiny_fp32", dict(T=1)),
+    ("tiny_fp32", dict(T=77)),
+    ("tiny_fp32", dict(T=300, E=1, k=1)),
+    ("tiny_fp32", dict(T=129, E=3, k=3)),
+    ("tiny_fp32", dict(T=200, capacity=20)),
+    ("tiny_fp32", dict(T=100, capacity=0)),
+    ("switch_top1", dict(T=1000)),
+    ("switch_top1", dict(T=333, E=5, d_model=136, d_ff=200)),
+    ("switch_top1", dict(T=700, capacity=3)),
+    ("noisy_top4", dict(T=515)),
+    ("noisy_top4", dict(T=64, E=8, k=8)),
+    ("noisy_top4", dict(T=250, E=1000, k=8, d_model=64, d_ff=64)),
+    ("gshard_top2", dict(T=1111, E=7, d_model=256, d_ff=1000)),
+    ("gshard_top2", dict(T=2048, capacity=17)),
+    ("dropless_top1", dict(T=999, d_model=512, d_ff=640)),
+]
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=[f"{n}-{'-'.join(f'{k}{v}' for k, v in o.items())}" for n, o in SMALL])
+def test_forward_small_shapes(moelib, dev, name, over):
+    c = _case(name, **over)
+    say(f"[forward-small] {c['cfg'].name} C={c['C']}")
+    fb = _run_forward(moelib, c, dev)
+    _check_forward(c, fb, np.arange(c["cfg"].T))
+
+
+def test_forward_empty_batch(moelib, dev):
+    import torch
+    from sparsely_gated_mixture_gate_amd.buffers import ForwardBuffers, to_device, to_numpy
+
+    cfg = scaled(CONFIGS["switch_top1"], T=8)
+    inp = make_inputs(cfg)
+    p = moelib.make_params(0, cfg.d_model, cfg.d_ff, cfg.E, cfg.k, cfg.dtype, cfg.act, False, 1.25)
+    fb = ForwardBuffers.alloc(p, dev)
+    d = {k: to_device(v) for k, v in inp.items()}
+    say("[forward-empty]")
+    moelib.moe_forward(p, d["x"], d["w_gate"], None, None, None, d["w1"], d["w2"], fb.y, fb.aux, fb.topk_idx,
+                       fb.topk_gate, fb.counts_routed, fb.counts_kept, fb.slot_dest, fb.ws)
+    torch.cuda.synchronize()
+    assert np.all(to_numpy(fb.counts_routed) == 0) and np.all(to_numpy(fb.counts_kept) == 0)
+
+
+def test_zero_gate_ties_and_identity_experts(moelib, dev):
+    """W_g = 0: every logit ties, expert 0 wins everywhere, capacity keeps the
+    first C tokens; identity experts make y = gate * x exactly checkable."""
+    import torch
+    from sparsely_gated_mixture_gate_amd.buffers import ForwardBuffers, to_device, to_numpy
+
+    cfg = scaled(CONFIGS["switch_top1"], T=3000)
+    inp = make_inputs(cfg, with_weights=False)
+    d, f, E = cfg.d_model, cfg.d_ff, cfg.E
+    inp["w_gate"] = np.zeros_like(inp["w_gate"])
+    w1 = np.zeros((E, d, f), np.float32)
+    w2 = np.zeros((E, f, d), np.float32)
+    w1[:, :, :d] = np.eye(d)
+    w1[:, :, d:2 * d] = -np.eye(d)
+    w2[:, :d, :] = np.eye(d)
+    w2[:, d:2 * d, :] = -np.eye(d)
+    inp["w1"], inp["w2"] = f32_to_bf16_bits(w1), f32_to_bf16_bits(w2)
+    C = 500
+    p = moelib.make_params(cfg.T, d, f, E, 1, "bf16", "gelu", False, 0.0, C)
+    fb = ForwardBuffers.alloc(p, dev)
+    dv = {k: to_device(v) for k, v in inp.items()}
+    say("[forward-ties-identity]")
+    moelib.moe_forward(p, dv["x"], dv["w_gate"], None, None, None, dv["w1"], dv["w2"], fb.y, fb.aux, fb.topk_idx,
+                       fb.topk_gate, fb.counts_routed, fb.counts_kept, fb.slot_dest, fb.ws)
+    torch.cuda.synchronize()
+    assert np.all(to_numpy(fb.topk_idx) == 0)
+    sd = to_numpy(fb.slot_dest)[:, 0]
+    assert np.array_equal(sd[:C], np.arange(C)) and np.all(sd[C:] == -1)
+    assert np.allclose(to_numpy(fb.topk_gate), 1.0 / E, rtol=1e-6)
+    x = as_f64(inp["x"], "bf16")
+    y = as_f64(to_numpy(fb.y), "bf16")
+    rel_rows_ok(y[:C], x[:C] / E, TOL["bf16"], "identity y")
+    assert np.all(y[C:] == 0.0)
+
+
+def test_forward_is_deterministic(moelib, dev):
+    from sparsely_gated_mixture_gate_amd.buffers import to_numpy
+
+    c = _case("noisy_top4", T=4000)
+    say("[determinism] noisy_top4 T=4000 x2")
+    a = _run_forward(moelib, c, dev)
+    b = _run_forward(moelib, c, dev)
+    for f in ("y", "aux", "topk_idx", "topk_gate", "counts_routed", "counts_kept", "slot_dest"):
+        x, y = to_numpy(getattr(a, f)), to_numpy(getattr(b, f))
+        assert x.tobytes() == y.tobytes(), f
