@@ -53,6 +53,11 @@ class moe_params(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    # torch ships its own HIP runtime (soname libamdhip64.so.7). Loading torch
+    # first makes libmoe.so bind to that same runtime instance, so the library
+    # and torch share one device context, its streams and its allocations.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     PP = ctypes.POINTER(moe_params)
