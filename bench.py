@@ -39,6 +39,12 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0, help="target CPU seconds for the oracle sample")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per expert-FFN launch measured with rocprofv3 counters")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain copy kernel of this size before timing (counter calibration)")
+    ap.add_argument("--pmc-report", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into --traffic-json")
+    ap.add_argument("--stats-report", metavar="KERNEL_STATS_CSV",
+                    help="print a rocprofv3 --stats kernel_stats.csv as a markdown table")
     return ap.parse_args()
 
 
@@ -101,8 +107,89 @@ def cpu_baseline(cfg, inp, budget_s):
     }
 
 
+def source_hash() -> str:
+    """Hash of the HIP sources: counter data taken on other sources is stale."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparsely_gated_mixture_gate_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_report(fetch_dir, write_dir, out_json, config, calib_mib):
+    """Per-launch HBM bytes of the expert FFN (GEMM1 + GEMM2 + tile map) from
+    two rocprofv3 --pmc runs, each scaled by what the counter reads for a
+    plain copy kernel of calib_mib MiB (which reads and writes that much)."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += list(csv.DictReader(open(f)))
+        out = {}
+        for r in rows:
+            if r.get("Counter_Name") != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+
+    def mean(d, pred):
+        vals = [v for k, vs in d.items() if pred(k) for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    is_copy = lambda k: "elementwise_kernel" in k and "MulFunctor" in k  # noqa: E731
+    kib = calib_mib * 1024.0
+    f_scale = kib / mean(fetch, is_copy)
+    w_scale = kib / mean(write, is_copy)
+    parts = {}
+    for tag, pred in (("gemm1", lambda k: "grouped_gemm" in k and "true>" in k),
+                      ("gemm2", lambda k: "grouped_gemm" in k and "false>" in k),
+                      ("tile_map", lambda k: "tile_map_kernel" in k)):
+        f_kib, w_kib = mean(fetch, pred), mean(write, pred)
+        parts[tag] = {"fetch_bytes": f_kib * 1024 * f_scale, "write_bytes": w_kib * 1024 * w_scale,
+                      "fetch_kib_raw": f_kib, "write_kib_raw": w_kib}
+    total = sum(p["fetch_bytes"] + p["write_bytes"] for p in parts.values())
+    try:
+        with open(out_json) as fh:
+            tj = json.load(fh)
+    except (OSError, ValueError):
+        tj = {}
+    tj["current_hash"] = source_hash()
+    tj[config] = {"source_hash": source_hash(), "bytes_per_launch": total, "parts": parts,
+                  "copy_calibration": {"mib": calib_mib, "fetch_scale": f_scale, "write_scale": w_scale}}
+    with open(out_json, "w") as fh:
+        json.dump(tj, fh, indent=1)
+    print(json.dumps(tj[config], indent=1))
+
+
+def stats_report(path):
+    import csv
+
+    rows = list(csv.DictReader(open(path)))
+    print("| kernel | calls | average us | min us | max us | share % |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for r in rows:
+        name = r["Name"].replace("moe::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+              f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+
+
 def main():
     args = parse()
+    if args.stats_report:
+        stats_report(args.stats_report)
+        return
+    if args.pmc_report:
+        pmc_report(args.pmc_report[0], args.pmc_report[1], args.traffic_json, args.config,
+                   args.copy_calibration_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -124,6 +211,12 @@ def main():
                         cfg.capacity_factor)
     fb = ForwardBuffers.alloc(p, dev)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def forward():
         moe.moe_forward(p, d["x"], d["w_gate"], d["gate_bias"], d["w_noise"], d["noise"], d["w1"], d["w2"], fb.y,
@@ -192,7 +285,7 @@ def main():
         with open(args.traffic_json) as fh:
             tj = json.load(fh)
         entry = tj.get(cfg.name)
-        if entry and entry.get("source_hash") == tj.get("current_hash"):
+        if entry and entry.get("source_hash") == source_hash():
             traffic = entry["bytes_per_launch"]
     except (OSError, ValueError):
         pass
