@@ -13,18 +13,21 @@
 //     ceil(rows_e / BM) M-tiles per expert; GEMM blocks binary-search it, so the
 //     host never synchronises on the ragged segment sizes. The grid is an upper
 //     bound (ceil(R_max / BM) + E M-tiles); surplus blocks exit at once.
-//   * bf16 path: 128x128x64 block tiles, 256 threads = 2x2 waves of 64x64, MFMA
-//     v_mfma_f32_16x16x32_bf16 with fp32 accumulation. A (activations, K
-//     contiguous) is copied to LDS in 16-byte chunks; B (weights [K][N], N
-//     contiguous) is loaded as 8x8 bf16 blocks and transposed in registers so
-//     both operands sit K-contiguous in LDS and each MFMA operand is one
-//     ds_read_b128. Rows of 8 chunks are XOR-swizzled (chunk ^ (row ^ row>>3) & 7)
-//     so fragment reads and tile writes are free of bank conflicts. Double-
-//     buffered LDS with global loads for tile k+1 in flight during the MFMAs of
-//     tile k. MFMA column c of N-subtile j of a wave maps to output column
-//     4c + j, so each lane ends with 4 consecutive columns per row and stores
-//     8 bytes; the activation (ReLU / exact GELU) is applied in fp32 before the
+//   * bf16 path: BM x 256 x 64 tiles (BM = 128 for experts of about one tile of
+//     rows, where the weights stream from HBM; 256 for large segments, where the
+//     MFMAs bound), 512 threads = 2 x 4 waves, MFMA v_mfma_f32_16x16x32_bf16 with
+//     fp32 accumulation. Both operands are copied to LDS in their HBM layout
+//     (16-byte chunks, XOR-swizzled per row against bank conflicts): activation
+//     rows K-contiguous, read as one ds_read_b128 per MFMA operand; weight rows
+//     N-contiguous, read K-contiguous with the gfx950 transposing load
+//     ds_read_b64_tr_b16 (two per operand). Double-buffered LDS with the next
+//     tiles' global loads in flight (register staging two k-tiles ahead). The MFMA runs with swapped
+//     operands (D = W^T A^T) so each lane ends with 4 consecutive output columns
+//     of a row (8-byte stores); ReLU / exact GELU is applied in fp32 before the
 //     bf16 (nearest-even) store.
+//   * scheduling: real tiles are dealt evenly to the 8 XCDs in contiguous
+//     chunks (tiles sharing an activation or weight panel share that XCD's L2),
+//     rastered inside each expert in groups of 4 M-tiles.
 //   * fp32 path: a plain LDS-tiled fp32 FMA kernel (64x64x16 tiles).
 #include "common.h"
 
@@ -33,8 +36,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-constexpr int BM = 128, BN = 128, BK = 64;
 
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets, int E, int bm,
                                                         int32_t* __restrict__ tile_start) {
@@ -68,135 +69,270 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ tile_start
   return true;
 }
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+constexpr int kXcds = 8;     // MI355X: 8 XCDs, workgroups dealt round-robin, one L2 each
+constexpr int kGroupM = 4;   // M-tiles per raster group inside an expert
+
+// Chunk swizzles (16-byte chunks). A rows hold BK/8 chunks: physical =
+// chunk ^ swz_a_rc(row) (below). B rows hold 32 chunks (256 bf16 of N):
+// physical = chunk ^ 2*swz_b(k); swz_b spreads the 8 rows that one half-wave
+// reads in a transposing load over 8 distinct 32-byte bank groups.
+__device__ __forceinline__ int swz_b(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+
+// Map this workgroup to (expert, M-tile rows, N-tile). Real tiles are spread
+// evenly over the XCDs in contiguous chunks (tiles that share an activation
+// panel or a weight panel then share an L2); inside an expert, tiles are
+// rastered in groups of kGroupM M-tiles so a wave of workgroups covers a compact
+// block of the output. Returns false for surplus workgroups.
+__device__ __forceinline__ bool schedule_tile(const int32_t* __restrict__ tile_start,
+                                              const int32_t* __restrict__ offsets, int E, int bm, int nt_count,
+                                              int* e_out, int* row0, int* row_end, int* nt_out) {
+  const int total = tile_start[E] * nt_count;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int b = blockIdx.x;
+  const int slot = b / kXcds;
+  const int L = (b % kXcds) * per + slot;
+  if (slot >= per || L >= total) return false;
+  const int mt_lin = L / nt_count;
+  int lo = 0, hi = E;  // tile_start[lo] <= mt_lin < tile_start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_start[mid] <= mt_lin) lo = mid; else hi = mid;
+  }
+  const int mt0 = tile_start[lo];
+  const int mts = tile_start[lo + 1] - mt0;
+  const int loc = L - mt0 * nt_count;
+  const int group = loc / (kGroupM * nt_count);
+  const int first = group * kGroupM;
+  const int gm = min(kGroupM, mts - first);
+  const int r = loc - group * kGroupM * nt_count;
+  const int mt = first + r % gm;
+  *nt_out = r / gm;
+  *e_out = lo;
+  *row0 = offsets[lo] + mt * bm;
+  *row_end = offsets[lo + 1];
+  return true;
+}
+
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for a raw byte range (stride 0, 32-bit data format); loads at
+// offsets >= num_bytes return zero.
+__device__ __forceinline__ int32x4 buffer_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  int32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)((a >> 32) & 0xFFFFu);
+  r[2] = (int)num_bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Asynchronous 16-byte load straight into LDS: lane l of the wave writes bytes
+// lds_base + 16*l .. +15. The load counts in vmcnt; it writes no VGPR, so nothing
+// in registers can be clobbered while it is in flight.
+__device__ __forceinline__ void load_to_lds(uint32_t lds_base, int voffset, const int32x4& rsrc, int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (expcnt / lgkmcnt not waited).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Wait until at most rem * LD of this thread's loads are in flight (rem = k-tiles
+// issued after the one about to be read).
+template <int LD, int MAXREM>
+__device__ __forceinline__ void wait_tiles(int rem) {
+  if constexpr (MAXREM >= 3) {
+    if (rem >= 3) { wait_vmcnt<3 * LD>(); return; }
+  }
+  if constexpr (MAXREM >= 2) {
+    if (rem >= 2) { wait_vmcnt<2 * LD>(); return; }
+  }
+  if constexpr (MAXREM >= 1) {
+    if (rem >= 1) { wait_vmcnt<LD>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+// Barrier without a memory fence (a fence would drain the in-flight prefetches);
+// the empty asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int RC>
+__device__ __forceinline__ int swz_a_rc(int row) {
+  if constexpr (RC == 8) {
+    return (row ^ (row >> 3)) & 7;
+  } else {
+    return (row >> 2) & 3;
+  }
+}
 
 // C[rows of segment e] = act?(A . W[e]); A [R][K], W [E][K][N], C [R][N], all bf16.
-template <int ACT, bool APPLY_ACT>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                                   const uint16_t* __restrict__ W,
-                                                                   uint16_t* __restrict__ C,
-                                                                   const int32_t* __restrict__ offsets,
-                                                                   const int32_t* __restrict__ tile_start, int E,
-                                                                   int K, int N, int n_tiles_n) {
-  __shared__ uint4 sA[2][BM * 8];
-  __shared__ uint4 sB[2][BN * 8];
+// BM x 256 x BK tiles, 512 threads = 2 x 4 waves of (BM/2) x 64, NSTAGE-deep
+// LDS ring fed by direct-to-LDS buffer loads (NSTAGE - 1 k-tiles in flight).
+template <int BM, int BK, int NSTAGE, int ACT, bool APPLY_ACT>
+__global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                                const uint16_t* __restrict__ W,
+                                                                uint16_t* __restrict__ C,
+                                                                const int32_t* __restrict__ offsets,
+                                                                const int32_t* __restrict__ tile_start, int E,
+                                                                int K, int N, int n_tiles_n) {
+  constexpr int BN = 256;
+  constexpr int WM = BM / 2;             // wave tile rows
+  constexpr int MI = WM / 16;            // 16-row MFMA tiles per wave
+  constexpr int NI = 4;                  // 16-column MFMA tiles per wave (64 columns)
+  constexpr int RC = BK / 8;             // 16-byte chunks per A row
+  constexpr int A_CH = BM * RC;          // chunks per A tile
+  constexpr int B_CH = BK * 32;          // chunks per B tile (256 columns = 32 chunks per row)
+  constexpr int A_LD = A_CH / 512;       // loads per thread per tile
+  constexpr int B_LD = B_CH / 512;
+  constexpr int LD = A_LD + B_LD;
+  constexpr int STAGE_CH = A_CH + B_CH;
+  static_assert(A_CH % 512 == 0 && B_CH % 512 == 0, "tile / thread mismatch");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 5, "stages");
+  __shared__ uint4 smem[NSTAGE * STAGE_CH];
+
+  int e, row0, row_end, nt;
+  if (!schedule_tile(tile_start, offsets, E, BM, n_tiles_n, &e, &row0, &row_end, &nt)) return;
   const int tid = threadIdx.x;
-  const int mt = blockIdx.x / n_tiles_n;
-  const int nt = blockIdx.x - mt * n_tiles_n;
-  int e, row0, row_end;
-  if (!find_tile(tile_start, offsets, E, mt, BM, &e, &row0, &row_end)) return;
-  const int n0 = nt * BN;
-  const uint16_t* __restrict__ We = W + (int64_t)e * K * N;
-
-  // global -> register staging
-  uint4 ra[4];
-  uint4 rb[8];
-  const bool b_loader = tid < 128;
-  const int b_kb = tid >> 4, b_nb = tid & 15;
-
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, kc = c & 7;
-      int grow = row0 + row;
-      grow = grow < row_end ? grow : row_end - 1;
-      const int gk = k0 + kc * 8;
-      ra[i] = gk < K ? *reinterpret_cast<const uint4*>(A + (int64_t)grow * K + gk) : make_uint4(0, 0, 0, 0);
-    }
-    if (b_loader) {
-      const int gn = n0 + b_nb * 8;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int gk = k0 + b_kb * 8 + r;
-        rb[r] = (gk < K && gn < N) ? *reinterpret_cast<const uint4*>(We + (int64_t)gk * N + gn)
-                                   : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, kc = c & 7;
-      sA[buf][row * 8 + (kc ^ swz(row))] = ra[i];
-    }
-    if (b_loader) {
-      // rb[r] holds k = 8*b_kb + r, n = 8*b_nb .. +7 (two per dword, low half = even n).
-      // Output row n (= 8*b_nb + i) needs k = 8*b_kb .. +7 (two per dword, low half = even k).
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(rb);  // w[4*r + q]: k=r, n=2q,2q+1
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = i >> 1;
-        const bool hi = i & 1;
-        uint4 o;
-        uint32_t d[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t lo_k = w[4 * (2 * p) + q];
-          const uint32_t hi_k = w[4 * (2 * p + 1) + q];
-          d[p] = hi ? ((lo_k >> 16) | (hi_k & 0xFFFF0000u)) : ((lo_k & 0xFFFFu) | (hi_k << 16));
-        }
-        o.x = d[0]; o.y = d[1]; o.z = d[2]; o.w = d[3];
-        const int row = b_nb * 8 + i;
-        sB[buf][row * 8 + (b_kb ^ swz(row))] = o;
-      }
-    }
-  };
-
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  floatx4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = nt * BN;
   const int nk = (K + BK - 1) / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile((kt + 1) * BK);
+  const int k_last = (nk - 1) * BK;
+  const bool k_tail = (K % BK) != 0;
+  const int rows = row_end - row0;
+
+  // Per-thread byte offsets, fixed for the whole K loop; the k-tile advances the
+  // wave-uniform soffset. Lane l fills LDS slot l of its wave's 64-chunk run, so it
+  // fetches the chunk that the XOR swizzle places in that slot. Rows past the
+  // segment are clamped (read, never stored). In the last, partial k-tile the A
+  // chunks past K are clamped inside the row (finite data) and the B rows past K
+  // (and B columns past N throughout) point outside the buffer, which loads zero.
+  const int32x4 rsA = buffer_rsrc(A + (int64_t)row0 * K, (uint32_t)rows * K * 2);
+  const int32x4 rsB = buffer_rsrc(W + (int64_t)e * K * N, (uint32_t)K * N * 2);
+  constexpr int kOut = 0x7FFFFFF0;  // byte offset past any operand (K*N*2 < 2^31 - 16 is checked on the host)
+  int voffA[A_LD], voffA_last[A_LD], voffB[B_LD], voffB_last[B_LD];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = ks * 4 + (lane >> 4);
-      bf16x8 af[4], bfr[4];
+  for (int i = 0; i < A_LD; ++i) {
+    const int c = tid + 512 * i;
+    const int row = c / RC, phys = c % RC;
+    const int kc = phys ^ swz_a_rc<RC>(row);
+    const int lrow = min(row, rows - 1);
+    voffA[i] = (lrow * K + kc * 8) * 2;
+    voffA_last[i] = (lrow * K + min(kc * 8, K - k_last - 8)) * 2;  // + soffset k_last*2
+  }
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int row = wm * 64 + mi * 16 + (lane & 15);
-        af[mi] = __builtin_bit_cast(bf16x8, sA[buf][row * 8 + (ch ^ swz(row))]);
-      }
+  for (int i = 0; i < B_LD; ++i) {
+    const int c = tid + 512 * i;
+    const int kr = c >> 5, phys = c & 31;
+    const int nc = phys ^ (2 * swz_b(kr));
+    const int gn = n0 + nc * 8;
+    voffB[i] = gn < N ? (kr * N + gn) * 2 : kOut;
+    voffB_last[i] = (gn < N && k_last + kr < K) ? (kr * N + gn) * 2 : kOut;
+  }
+  typedef __attribute__((address_space(3))) uint4 lds_uint4;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_uint4*)(&smem[0]);
+
+  auto issue = [&](int kt) {
+    const int st = kt % NSTAGE;
+    const bool last = k_tail && kt == nk - 1;
+    const int soffA = kt * BK * 2;
+    const int soffB = kt * BK * N * 2;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int nrow = wn * 64 + (lane & 15) * 4 + ni;
-        bfr[ni] = __builtin_bit_cast(bf16x8, sB[buf][nrow * 8 + (ch ^ swz(nrow))]);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    for (int i = 0; i < A_LD; ++i) {
+      const uint32_t dst = lds0 + (uint32_t)((st * STAGE_CH + i * 512 + wave * 64) * 16);
+      load_to_lds(__builtin_amdgcn_readfirstlane(dst), last ? voffA_last[i] : voffA[i], rsA, soffA);
     }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const uint32_t dst = lds0 + (uint32_t)((st * STAGE_CH + A_CH + i * 512 + wave * 64) * 16);
+      load_to_lds(__builtin_amdgcn_readfirstlane(dst), last ? voffB_last[i] : voffB[i], rsB, soffB);
+    }
+  };
+
+  const int wm = wave >> 2, wn = wave & 3;
+  const int g = lane >> 4;   // k-group of 8 inside a 32-wide k step
+  const int s = lane & 15;
+  floatx4 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](int st) {
+    const uint4* sA = &smem[st * STAGE_CH];
+    typedef __attribute__((address_space(3))) char lds_char;
+    lds_char* sB = (lds_char*)(&smem[st * STAGE_CH + A_CH]);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8 af[MI], bfr[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = wm * WM + mi * 16 + s;
+        const int ch = ks * 4 + g;
+        af[mi] = __builtin_bit_cast(bf16x8, sA[row * RC + (ch ^ swz_a_rc<RC>(row))]);
+      }
+      // Transposing LDS read: source lane s of each 16-lane group points at row
+      // k0 + s/4, columns n + 4*(s%4) .. +3; lane L of the group then receives
+      // W[k0 .. k0+3][n + L]. Two reads give the 8 k-values of a bf16 operand.
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int krow = ks * 32 + 8 * g + (s >> 2);
+        const int ncol = wn * 64 + ni * 16 + 4 * (s & 3);
+        const int c = ncol >> 3;
+        const int b0 = krow * 512 + ((c ^ (2 * swz_b(krow))) << 4) + ((ncol & 7) << 1);
+        const int b1 = (krow + 4) * 512 + ((c ^ (2 * swz_b(krow + 4))) << 4) + ((ncol & 7) << 1);
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b0));
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b1));
+        const short __attribute__((ext_vector_type(8))) both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        bfr[ni] = __builtin_bit_cast(bf16x8, both);
+      }
+      // swapped operands: D[n][m] = sum_k W[k][n] A[m][k], so each lane ends with
+      // 4 consecutive output columns of one row
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int t = 0; t < NSTAGE - 1; ++t)
+    if (t < nk) issue(t);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_tiles<LD, NSTAGE - 2>(min(NSTAGE - 2, nk - 1 - kt));
+    block_barrier();  // tile kt is in LDS for every wave; buffer of tile kt-1 is free
+    if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1);
+    compute(kt % NSTAGE);
   }
 
-  // epilogue: lane holds rows 4*(lane>>4)+j of each 16-row subtile and columns
-  // 4*(lane&15) + ni (ni = 0..3) of the wave's 64 columns.
-  const int gcol = n0 + wn * 64 + (lane & 15) * 4;
-  if (gcol >= N) return;
+  // epilogue: lane holds C[m = .. + s][n = .. + 4g + j], j = 0..3, per MFMA tile
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+  for (int mi = 0; mi < MI; ++mi) {
+    const int grow = row0 + wm * WM + mi * 16 + s;
+    if (grow >= row_end) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int grow = row0 + wm * 64 + mi * 16 + (lane >> 4) * 4 + j;
-      if (grow >= row_end) continue;
+    for (int ni = 0; ni < NI; ++ni) {
+      const int gcol = n0 + wn * 64 + ni * 16 + 4 * g;
+      if (gcol >= N) continue;
       float v[4];
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) v[ni] = APPLY_ACT ? activation<ACT>(acc[mi][ni][j]) : acc[mi][ni][j];
+      for (int j = 0; j < 4; ++j) v[j] = APPLY_ACT ? activation<ACT>(acc[mi][ni][j]) : acc[mi][ni][j];
       uint2 o;
       o.x = pack_bf16x2(v[0], v[1]);
       o.y = pack_bf16x2(v[2], v[3]);
@@ -262,33 +398,51 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
   }
 }
 
-template <int ACT>
-hipError_t launch_ffn_act(const FfnLaunch& a, hipStream_t s) {
-  const int bm = a.dtype == 1 ? BM : 64;
-  const int bn = a.dtype == 1 ? BN : 64;
-  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, bm, a.tile_start);
+template <int BM, int BK, int NSTAGE, int ACT>
+hipError_t launch_bf16(const FfnLaunch& a, hipStream_t s) {
+  constexpr int BN = 256;
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, BM, a.tile_start);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t mtiles = (a.max_rows + bm - 1) / bm + a.E;
-  const int nt1 = (a.f + bn - 1) / bn, nt2 = (a.d + bn - 1) / bn;
-  if (a.dtype == 1) {
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<ACT, true>), dim3((unsigned)(mtiles * nt1)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(a.x_perm), static_cast<const uint16_t*>(a.w1),
-                       static_cast<uint16_t*>(a.h1), a.offsets, a.tile_start, a.E, a.d, a.f, nt1);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<ACT, false>), dim3((unsigned)(mtiles * nt2)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(a.h1), static_cast<const uint16_t*>(a.w2),
-                       static_cast<uint16_t*>(a.y_perm), a.offsets, a.tile_start, a.E, a.f, a.d, nt2);
-  } else {
-    hipLaunchKernelGGL((grouped_gemm_f32_kernel<ACT, true>), dim3((unsigned)(mtiles * nt1)), dim3(256), 0, s,
-                       static_cast<const float*>(a.x_perm), static_cast<const float*>(a.w1),
-                       static_cast<float*>(a.h1), a.offsets, a.tile_start, a.E, a.d, a.f, nt1);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((grouped_gemm_f32_kernel<ACT, false>), dim3((unsigned)(mtiles * nt2)), dim3(256), 0, s,
-                       static_cast<const float*>(a.h1), static_cast<const float*>(a.w2),
-                       static_cast<float*>(a.y_perm), a.offsets, a.tile_start, a.E, a.f, a.d, nt2);
-  }
+  const int64_t mtiles = (a.max_rows + BM - 1) / BM + a.E;
+  const int nt1 = (a.f + BN - 1) / BN, nt2 = (a.d + BN - 1) / BN;
+  auto grid = [](int64_t tiles) { return dim3((unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds)); };
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BK, NSTAGE, ACT, true>), grid(mtiles * nt1), dim3(512), 0, s,
+                     static_cast<const uint16_t*>(a.x_perm), static_cast<const uint16_t*>(a.w1),
+                     static_cast<uint16_t*>(a.h1), a.offsets, a.tile_start, a.E, a.d, a.f, nt1);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BK, NSTAGE, ACT, false>), grid(mtiles * nt2), dim3(512), 0, s,
+                     static_cast<const uint16_t*>(a.h1), static_cast<const uint16_t*>(a.w2),
+                     static_cast<uint16_t*>(a.y_perm), a.offsets, a.tile_start, a.E, a.f, a.d, nt2);
   return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_f32(const FfnLaunch& a, hipStream_t s) {
+  constexpr int TB = 64;
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, TB, a.tile_start);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t mtiles = (a.max_rows + TB - 1) / TB + a.E;
+  const int nt1 = (a.f + TB - 1) / TB, nt2 = (a.d + TB - 1) / TB;
+  hipLaunchKernelGGL((grouped_gemm_f32_kernel<ACT, true>), dim3((unsigned)(mtiles * nt1)), dim3(256), 0, s,
+                     static_cast<const float*>(a.x_perm), static_cast<const float*>(a.w1),
+                     static_cast<float*>(a.h1), a.offsets, a.tile_start, a.E, a.d, a.f, nt1);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL((grouped_gemm_f32_kernel<ACT, false>), dim3((unsigned)(mtiles * nt2)), dim3(256), 0, s,
+                     static_cast<const float*>(a.h1), static_cast<const float*>(a.w2),
+                     static_cast<float*>(a.y_perm), a.offsets, a.tile_start, a.E, a.f, a.d, nt2);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_ffn_act(const FfnLaunch& a, hipStream_t s) {
+  if (a.dtype != 1) return launch_f32<ACT>(a, s);
+  // Expected rows per expert decides the M tile: weight-streaming experts
+  // (about one tile of rows each) take 128-row tiles, large segments 256.
+  const int64_t rows_per_expert = a.max_rows / a.E;
+  if (rows_per_expert >= 512) return launch_bf16<256, 32, 4, ACT>(a, s);
+  return launch_bf16<128, 64, 3, ACT>(a, s);
 }
 
 }  // namespace

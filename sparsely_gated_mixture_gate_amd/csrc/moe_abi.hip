@@ -53,6 +53,12 @@ moe_status check_params(const moe_params* p) {
   if (p->T * (int64_t)p->k >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*k = %lld >= 2^31", (long long)(p->T * p->k));
   if (isnan(p->capacity_factor)) return fail(MOE_ERR_INVALID_ARG, "capacity_factor is NaN");
+  // 32-bit byte offsets inside one expert's weights and one row segment
+  const int64_t elt = p->dtype == MOE_BF16 ? 2 : 4;
+  const int64_t widest = p->d_model > p->d_ff ? p->d_model : p->d_ff;
+  if ((int64_t)p->d_model * p->d_ff * elt >= (int64_t(1) << 31) - 16 ||
+      p->T * (int64_t)p->k * widest * elt >= (int64_t(1) << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "an expert's weights or the permuted rows exceed 32-bit byte offsets");
   return MOE_OK;
 }
 
