@@ -51,6 +51,8 @@ struct RouteLaunch {
   float* aux_out;
   float* logits_out;
   // workspace pieces
+  float* w32;        // [d][epad] fp32 gate weights
+  float* wn32;       // [d][epad] fp32 noise weights (noisy gate)
   float* part_prob;  // [E][nblk]
   float* part_imp;   // [E][nblk]
   float* part_load;  // [E][nblk]
@@ -58,6 +60,7 @@ struct RouteLaunch {
   double* red;       // [3][E]
 };
 int route_tokens_per_block(int E, bool noisy);
+size_t route_weight_floats(int d, int E);
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
 
 struct DispatchLaunch {

@@ -93,6 +93,7 @@ struct Carver {
 };
 
 struct RouteWs {
+  float *w32, *wn32;
   float *part_prob, *part_imp, *part_load;
   int32_t* part_cnt;
   double* red;
@@ -102,6 +103,8 @@ RouteWs carve_route(Carver& c, const moe_params* p, bool noisy) {
   const int64_t nblk = (p->T + tpb - 1) / tpb;
   const size_t n = (size_t)p->E * (size_t)(nblk > 0 ? nblk : 1);
   RouteWs w;
+  w.w32 = c.take<float>(route_weight_floats(p->d_model, p->E));
+  w.wn32 = noisy ? c.take<float>(route_weight_floats(p->d_model, p->E)) : nullptr;
   w.part_prob = c.take<float>(n);
   w.part_imp = c.take<float>(n);
   w.part_load = c.take<float>(n);
@@ -211,6 +214,8 @@ moe_status run_route(const moe_params* p, const void* x, const void* w_gate, con
   a.counts_routed = counts_routed;
   a.aux_out = aux_out;
   a.logits_out = logits_out;
+  a.w32 = w.w32;
+  a.wn32 = w.wn32;
   a.part_prob = w.part_prob;
   a.part_imp = w.part_imp;
   a.part_load = w.part_load;

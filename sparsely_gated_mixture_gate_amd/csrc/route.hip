@@ -11,16 +11,19 @@
 //
 // Design (gfx950): the gate GEMM is fp32 FMA in a fixed order -- each logit
 // accumulates x[t,j] * W[j,e] from +0 for j ascending, one fma per term -- so
-// the integer routing is reproducible bit-for-bit. A wave owns TM tokens and
-// all experts (expert e = lane + 64*c lives in register c of lane e % 64).
-// The TM tokens are wave-uniform, so x is read with scalar loads and feeds the
-// FMA as a scalar operand; only W_g is staged in LDS (converted to fp32 once
-// per block). Softmax statistics and the top-(k+1) selection are wave
-// reductions over registers (butterfly shuffles; the comparison order is
-// value descending, expert index ascending), so the [T,E] logits never touch
-// LDS or HBM unless the caller asks for them. Per-block partial sums of the
-// probabilities, gates, load estimates and counts go to the workspace and are
-// reduced in a fixed order by route_reduce / route_aux (deterministic).
+// the integer routing is reproducible bit-for-bit. A block holds 64 tokens, one
+// per lane, and E/EPW waves; wave w owns experts [w*EPW, (w+1)*EPW). A small
+// prep kernel widens W_gate (and W_noise) to fp32 once per call; inside the
+// loop each weight row slice is wave-uniform, arrives by scalar loads and is the
+// scalar operand of v_fmac_f32, while each lane's x row arrives by 16-byte
+// vector loads (bf16 widened once per value). Each wave then keeps its top-(k+1)
+// candidates and softmax statistics (max, sum of exp) per token in LDS; one wave
+// merges them (candidates by value descending, expert index ascending; sums
+// rescaled to the common max in wave order) into the top-k, the gates and the
+// thresholds of the load estimator; every wave then reduces its experts'
+// probabilities, gates, counts and load estimates over the 64 tokens with
+// butterfly shuffles. Per-block partial sums go to the workspace and are reduced
+// in a fixed order by route_reduce / route_aux (deterministic, no float atomics).
 #include <float.h>
 
 #include "common.h"
@@ -86,11 +89,11 @@ __device__ __forceinline__ bool better(float v, int e, float bv, int be) { retur
 
 struct RouteArgs {
   int64_t T;
-  int d, E, k, kk, renormalize, bk, nblk;
+  int d, E, epad, k, kk, renormalize, nblk, nw;
   const void* x;
-  const void* w_gate;
+  const float* w32;   // [d][epad] fp32 copy of W_gate (zero columns past E)
+  const float* wn32;  // [d][epad] fp32 copy of W_noise, or null
   const float* gate_bias;
-  const void* w_noise;
   const float* noise;
   int32_t* topk_idx;
   float* topk_gate;
@@ -102,181 +105,182 @@ struct RouteArgs {
 };
 
 template <typename Tin>
-__device__ __forceinline__ float load_elem(const Tin* p, int64_t i) {
-  if constexpr (sizeof(Tin) == 2) {
-    return bf16_to_f32(p[i]);
-  } else {
-    return p[i];
+__global__ __launch_bounds__(256) void route_prep_kernel(const Tin* __restrict__ w, float* __restrict__ w32,
+                                                         int d, int E, int epad) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)d * epad) return;
+  const int64_t j = i / epad;
+  const int e = (int)(i - j * epad);
+  float v = 0.0f;
+  if (e < E) {
+    if constexpr (sizeof(Tin) == 2) {
+      v = bf16_to_f32(w[j * E + e]);
+    } else {
+      v = w[j * E + e];
+    }
   }
+  w32[i] = v;
 }
 
-// Eight consecutive x values of one row (wave-uniform address, 16-byte aligned).
-template <typename Tin>
-__device__ __forceinline__ void load_x8(const Tin* __restrict__ row, int j, float* out) {
-  if constexpr (sizeof(Tin) == 2) {
-    const uint4 w = *reinterpret_cast<const uint4*>(row + j);
-    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
-    out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
-    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z);
-    out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
-  } else {
-    const float4 a = *reinterpret_cast<const float4*>(row + j);
-    const float4 b = *reinterpret_cast<const float4*>(row + j + 4);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
-  }
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;  // identical on every lane: each butterfly step adds the same two values
 }
 
-template <typename Tin, bool NOISY, int TN, int TM>
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-  constexpr int EP = 64 * TN;
+// One block = 64 tokens (one per lane) x all experts; wave w owns experts
+// [w*EPW, (w+1)*EPW). Each lane accumulates its token's logits for the wave's
+// experts as fixed ascending-j fma chains: x arrives per lane (16-byte vector
+// loads, unpacked once) and the fp32 weight row W[j][e0 .. e0+EPW) is
+// wave-uniform, read with scalar loads and used as the scalar FMA operand.
+template <typename Tin, bool NOISY, int EPW>
+__global__ __launch_bounds__(1024) void route_kernel(RouteArgs a) {
   extern __shared__ float smem[];
   const Tin* __restrict__ x = static_cast<const Tin*>(a.x);
-  const Tin* __restrict__ wg = static_cast<const Tin*>(a.w_gate);
-  const Tin* __restrict__ wn = static_cast<const Tin*>(a.w_noise);
-  const int d = a.d, E = a.E, k = a.k, kk = a.kk, BK = a.bk;
+  const float* __restrict__ w32 = a.w32;
+  const float* __restrict__ wn32 = a.wn32;
+  const int d = a.d, E = a.E, k = a.k, kk = a.kk, nw = a.nw, epad = a.epad;
   const int64_t T = a.T;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t t0 = (int64_t)blockIdx.x * (4 * TM) + wave * TM;
+  const int e0 = wave * EPW;
+  const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+  const bool tok_ok = t < T;
+  const Tin* __restrict__ xrow = x + (tok_ok ? t : T - 1) * d;  // rows past T: computed, never stored
 
-  float* wg_s = smem;
-  float* wn_s = smem + BK * EP;
-
-  float acc[TM][TN];
-  float accn[TM][TN];
+  float acc[EPW], accn[EPW];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int c = 0; c < TN; ++c) acc[i][c] = accn[i][c] = 0.0f;
+  for (int c = 0; c < EPW; ++c) acc[c] = accn[c] = 0.0f;
 
-  const Tin* xrow[TM];
+  // x chunks are prefetched one 8-wide step ahead
+  constexpr int XW = sizeof(Tin) == 2 ? 1 : 2;  // 16-byte words per 8 values
+  uint4 xn[XW];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t t = t0 + i < T ? t0 + i : T - 1;  // rows past T: computed, never stored
-    xrow[i] = x + t * d;
-  }
-
-  // ---- gate GEMM: fixed ascending-j fma chains --------------------------------
-  for (int j0 = 0; j0 < d; j0 += BK) {
-    const int jn = min(BK, d - j0);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < jn * EP; idx += 256) {
-      const int jj = idx / EP;
-      const int e = idx - jj * EP;
-      const int64_t gi = (int64_t)(j0 + jj) * E + e;
-      wg_s[idx] = e < E ? load_elem(wg, gi) : 0.0f;
-      if constexpr (NOISY) wn_s[idx] = e < E ? load_elem(wn, gi) : 0.0f;
+  for (int q = 0; q < XW; ++q) xn[q] = reinterpret_cast<const uint4*>(xrow)[q];
+  for (int j = 0; j < d; j += 8) {
+    uint4 xc[XW];
+#pragma unroll
+    for (int q = 0; q < XW; ++q) xc[q] = xn[q];
+    if (j + 8 < d) {
+#pragma unroll
+      for (int q = 0; q < XW; ++q) xn[q] = reinterpret_cast<const uint4*>(xrow + j + 8)[q];
     }
-    __syncthreads();
-    for (int jj = 0; jj < jn; jj += 8) {
-      float xv[TM][8];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) load_x8(xrow[i], j0 + jj, xv[i]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        float w[TN];
-#pragma unroll
-        for (int c = 0; c < TN; ++c) w[c] = wg_s[(jj + u) * EP + lane + 64 * c];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int c = 0; c < TN; ++c) acc[i][c] = __builtin_fmaf(xv[i][u], w[c], acc[i][c]);
-        if constexpr (NOISY) {
-          float wv[TN];
-#pragma unroll
-          for (int c = 0; c < TN; ++c) wv[c] = wn_s[(jj + u) * EP + lane + 64 * c];
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int c = 0; c < TN; ++c) accn[i][c] = __builtin_fmaf(xv[i][u], wv[c], accn[i][c]);
-        }
-      }
+    float xv[8];
+    if constexpr (sizeof(Tin) == 2) {
+      xv[0] = bf16_lo(xc[0].x); xv[1] = bf16_hi(xc[0].x);
+      xv[2] = bf16_lo(xc[0].y); xv[3] = bf16_hi(xc[0].y);
+      xv[4] = bf16_lo(xc[0].z); xv[5] = bf16_hi(xc[0].z);
+      xv[6] = bf16_lo(xc[0].w); xv[7] = bf16_hi(xc[0].w);
+    } else {
+      xv[0] = __uint_as_float(xc[0].x); xv[1] = __uint_as_float(xc[0].y);
+      xv[2] = __uint_as_float(xc[0].z); xv[3] = __uint_as_float(xc[0].w);
+      xv[4] = __uint_as_float(xc[XW - 1].x); xv[5] = __uint_as_float(xc[XW - 1].y);
+      xv[6] = __uint_as_float(xc[XW - 1].z); xv[7] = __uint_as_float(xc[XW - 1].w);
     }
-  }
-
-  // ---- per token: logits, top-(k+1), softmax, gates, partial sums -------------
-  float s_prob[TN], s_imp[TN], s_load[TN], s_cnt[TN];
 #pragma unroll
-  for (int c = 0; c < TN; ++c) s_prob[c] = s_imp[c] = s_load[c] = s_cnt[c] = 0.0f;
-
+    for (int u = 0; u < 8; ++u) {
+      const float* __restrict__ wrow = w32 + (int64_t)(j + u) * epad + e0;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t t = t0 + i;
-    if (t >= T) break;  // wave-uniform
-    float h[TN], cl[TN], sg[TN];
-#pragma unroll
-    for (int c = 0; c < TN; ++c) {
-      const int e = lane + 64 * c;
-      const bool valid = e < E;
-      float cv = acc[i][c];
-      if (a.gate_bias && valid) cv = cv + a.gate_bias[e];
-      cl[c] = cv;
+      for (int c = 0; c < EPW; ++c) acc[c] = __builtin_fmaf(xv[u], wrow[c], acc[c]);
       if constexpr (NOISY) {
-        sg[c] = canon_softplus(accn[i][c]);
-        h[c] = valid ? __builtin_fmaf(a.noise[t * E + e], sg[c], cv) : -INFINITY;
-      } else {
-        sg[c] = 1.0f;
-        h[c] = valid ? cv : -INFINITY;
+        const float* __restrict__ nrow = wn32 + (int64_t)(j + u) * epad + e0;
+#pragma unroll
+        for (int c = 0; c < EPW; ++c) accn[c] = __builtin_fmaf(xv[u], nrow[c], accn[c]);
       }
-      if (a.logits_out && valid) a.logits_out[t * E + e] = h[c];
     }
+  }
 
-    // top-kk: kk rounds of a wave-wide arg-max over the untaken experts
-    uint32_t taken = 0, taken_k = 0;
-    float sel_v[9];
-    int sel_e[9];
-    float thr_out = 0.0f, thr_in = 0.0f;  // k-th and (k+1)-th largest H
+  // ---- logits of this wave's experts ----------------------------------------
+  float h[EPW], cl[EPW], sg[EPW];
+#pragma unroll
+  for (int c = 0; c < EPW; ++c) {
+    const int e = e0 + c;
+    const bool valid = e < E;
+    float cv = acc[c];
+    if (a.gate_bias && valid) cv = cv + a.gate_bias[e];
+    cl[c] = cv;
+    if constexpr (NOISY) {
+      sg[c] = canon_softplus(accn[c]);
+      h[c] = valid ? __builtin_fmaf(a.noise[(tok_ok ? t : T - 1) * E + e], sg[c], cv) : -INFINITY;
+    } else {
+      sg[c] = 1.0f;
+      h[c] = valid ? cv : -INFINITY;
+    }
+    if (a.logits_out && valid && tok_ok) a.logits_out[t * E + e] = h[c];
+  }
+
+  // ---- wave-local top-kk candidates and softmax statistics -------------------
+  // LDS: cand_v/cand_i [nw][kk][64], wmax/wsum [nw][64], results per token.
+  float* cand_v = smem;
+  int* cand_i = reinterpret_cast<int*>(smem + nw * kk * 64);
+  float* wmax = smem + 2 * nw * kk * 64;
+  float* wsum = wmax + nw * 64;
+  float* res = wsum + nw * 64;  // [5 + 2*8][64]: m, 1/S, thr_out, thr_in, have_in, sel[8], gate[8]
+  {
+    uint64_t taken = 0;
+    float m_w = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 9; ++r) {
       if (r >= kk) break;
-      float bv = -INFINITY;
-      int be = 0x7FFFFFFF;
+      float best = -INFINITY;
+      int bi = -1;
 #pragma unroll
-      for (int c = 0; c < TN; ++c) {
-        const int e = lane + 64 * c;
-        if (e < E && !((taken >> c) & 1u) && (be == 0x7FFFFFFF || better(h[c], e, bv, be))) {
-          bv = h[c];
-          be = e;
+      for (int c = 0; c < EPW; ++c) {
+        if (e0 + c < E && !((taken >> c) & 1ull) && (bi < 0 || h[c] > best)) {  // strict '>': lower index on ties
+          best = h[c];
+          bi = c;
         }
       }
+      if (bi >= 0) taken |= 1ull << bi;
+      if (r == 0) m_w = best;
+      cand_v[(wave * kk + r) * 64 + lane] = best;
+      cand_i[(wave * kk + r) * 64 + lane] = bi >= 0 ? e0 + bi : 0x7FFFFFFF;
+    }
+    float s_w = 0.0f;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oe = __shfl_xor(be, off);
-        if (oe != 0x7FFFFFFF && (be == 0x7FFFFFFF || better(ov, oe, bv, be))) {
-          bv = ov;
-          be = oe;
+    for (int c = 0; c < EPW; ++c)
+      if (e0 + c < E) s_w += expf(h[c] - m_w);
+    wmax[wave * 64 + lane] = m_w;
+    wsum[wave * 64 + lane] = s_w;
+  }
+  __syncthreads();
+
+  // ---- merge (wave 0): global top-kk, softmax, gates --------------------------
+  if (wave == 0) {
+    float sel_v[9];
+    int sel_i[9];
+    float pv = INFINITY;
+    int pi = -1;
+#pragma unroll
+    for (int r = 0; r < 9; ++r) {
+      if (r >= kk) break;
+      float best = -INFINITY;
+      int bi = 0x7FFFFFFF;
+      for (int q = 0; q < nw * kk; ++q) {
+        const float v = cand_v[q * 64 + lane];
+        const int i = cand_i[q * 64 + lane];
+        if (i == 0x7FFFFFFF) continue;
+        if (!(v < pv || (v == pv && i > pi))) continue;  // already taken: not after the previous pick
+        if (bi == 0x7FFFFFFF || better(v, i, best, bi)) {
+          best = v;
+          bi = i;
         }
       }
-      sel_v[r] = bv;
-      sel_e[r] = be;
-      if (r == k - 1) thr_out = bv;
-      if (r == k) thr_in = bv;
-      if ((be & 63) == lane) {
-        taken |= 1u << (be >> 6);
-        if (r < k) taken_k |= 1u << (be >> 6);
-      }
+      sel_v[r] = best;
+      sel_i[r] = bi;
+      pv = best;
+      pi = bi;
     }
-
-    // softmax over all experts
-    const float m = sel_v[0];
-    float ex[TN];
-    float zs = 0.0f;
-#pragma unroll
-    for (int c = 0; c < TN; ++c) {
-      ex[c] = (lane + 64 * c < E) ? expf(h[c] - m) : 0.0f;
-      zs += ex[c];
+    float m = -INFINITY;
+    for (int w = 0; w < nw; ++w) m = fmaxf(m, wmax[w * 64 + lane]);
+    float S = 0.0f;
+    for (int w = 0; w < nw; ++w) {
+      const float mw = wmax[w * 64 + lane];
+      if (mw != -INFINITY) S += wsum[w * 64 + lane] * expf(mw - m);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) zs += __shfl_xor(zs, off);  // identical on every lane
-    const float inv_z = 1.0f / zs;
-
-    // gate values of the k kept experts (wave-uniform)
     float g[8];
     if (a.renormalize) {
-      float den = 0.0f;
-      float num[8];
+      float den = 0.0f, num[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         if (s >= k) break;
@@ -292,72 +296,79 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         if (s >= k) break;
-        g[s] = expf(sel_v[s] - m) / zs;
+        g[s] = expf(sel_v[s] - m) / S;
       }
     }
+    float thr_out = 0.0f, thr_in = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 9; ++r) {
+      if (r == k - 1) thr_out = sel_v[r];
+      if (r == k && r < kk) thr_in = sel_v[r];
+    }
+    res[0 * 64 + lane] = m;
+    res[1 * 64 + lane] = 1.0f / S;
+    res[2 * 64 + lane] = thr_out;
+    res[3 * 64 + lane] = thr_in;
+    res[4 * 64 + lane] = S;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       if (s >= k) break;
-      if (lane == s) {
-        a.topk_idx[t * k + s] = sel_e[s];
+      reinterpret_cast<int*>(res)[(5 + s) * 64 + lane] = sel_i[s];
+      res[(13 + s) * 64 + lane] = g[s];
+      if (tok_ok) {
+        a.topk_idx[t * k + s] = sel_i[s];
         a.topk_gate[t * k + s] = g[s];
       }
     }
+  }
+  __syncthreads();
 
-    // partial sums for the losses
-    const bool have_in = kk > k;
+  // ---- per-expert partial sums over the block's tokens ------------------------
+  const float m = res[0 * 64 + lane];
+  const float S = res[4 * 64 + lane];
+  const float thr_out = res[2 * 64 + lane];
+  const float thr_in = res[3 * 64 + lane];
+  const bool have_in = kk > k;
+  int sel[8];
+  float gs[8];
 #pragma unroll
-    for (int c = 0; c < TN; ++c) {
-      const int e = lane + 64 * c;
-      if (e >= E) continue;
-      s_prob[c] += ex[c] * inv_z;
-      const bool in_k = (taken_k >> c) & 1u;
-      if (in_k) {
-        s_cnt[c] += 1.0f;
+  for (int s = 0; s < 8; ++s) {
+    if (s >= k) break;
+    sel[s] = reinterpret_cast<const int*>(res)[(5 + s) * 64 + lane];
+    gs[s] = res[(13 + s) * 64 + lane];
+  }
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          if (s >= k) break;
-          if (sel_e[s] == e) s_imp[c] += g[s];
+  for (int c = 0; c < EPW; ++c) {
+    const int e = e0 + c;
+    const bool valid = e < E && tok_ok;
+    float p = 0.0f, imp = 0.0f, cnt = 0.0f, ld = 0.0f;
+    if (valid) {
+      p = expf(h[c] - m) / S;
+      bool in_k = false;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (s >= k) break;
+        if (sel[s] == e) {
+          in_k = true;
+          imp = gs[s];
         }
       }
+      cnt = in_k ? 1.0f : 0.0f;
       if constexpr (NOISY) {
-        float p;
-        if (in_k && !have_in) {
-          p = 1.0f;
-        } else {
-          p = std_normal_cdf((cl[c] - (in_k ? thr_in : thr_out)) / sg[c]);
-        }
-        s_load[c] += p;
+        ld = (in_k && !have_in) ? 1.0f : std_normal_cdf((cl[c] - (in_k ? thr_in : thr_out)) / sg[c]);
       }
     }
-  }
-
-  // ---- block partials: waves combined in a fixed order ------------------------
-  __syncthreads();
-  float* red = smem;  // [4 quantities][4 waves][EP]
-#pragma unroll
-  for (int c = 0; c < TN; ++c) {
-    const int e = lane + 64 * c;
-    red[(0 * 4 + wave) * EP + e] = s_prob[c];
-    red[(1 * 4 + wave) * EP + e] = s_imp[c];
-    red[(2 * 4 + wave) * EP + e] = s_load[c];
-    red[(3 * 4 + wave) * EP + e] = s_cnt[c];
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) {
-    float q[4];
-#pragma unroll
-    for (int qi = 0; qi < 4; ++qi) {
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) s += red[(qi * 4 + w) * EP + e];
-      q[qi] = s;
+    p = wave_sum(p);
+    imp = wave_sum(imp);
+    cnt = wave_sum(cnt);
+    if constexpr (NOISY) ld = wave_sum(ld);
+    if (lane == c && e < E) {
+      const int64_t o = (int64_t)e * a.nblk + blockIdx.x;
+      a.part_prob[o] = p;
+      a.part_imp[o] = imp;
+      a.part_load[o] = ld;
+      a.part_cnt[o] = (int32_t)cnt;
     }
-    const int64_t o = (int64_t)e * a.nblk + blockIdx.x;
-    a.part_prob[o] = q[0];
-    a.part_imp[o] = q[1];
-    a.part_load[o] = q[2];
-    a.part_cnt[o] = (int32_t)q[3];
   }
 }
 
@@ -450,79 +461,71 @@ __global__ void softplus_kernel(const float* __restrict__ z, float* __restrict__
   if (i < n) out[i] = canon_softplus(z[i]);
 }
 
-void route_shape(int E, bool noisy, int* tn, int* tm) {
-  int t = 1;
-  while (64 * t < E) t *= 2;
-  int m;
-  switch (t) {
-    case 1: m = 8; break;
-    case 2: m = 8; break;
-    case 4: m = 4; break;
-    case 8: m = 2; break;
-    default: m = 1; break;
-  }
-  if (noisy && m > 1) m /= 2;
-  *tn = t;
-  *tm = m;
-}
+int route_epw(int E) { return E <= 256 ? 16 : (E <= 512 ? 32 : 64); }
 
-template <typename Tin, bool NOISY, int TN, int TM>
+template <typename Tin, bool NOISY, int EPW>
 hipError_t launch_route_t(const RouteArgs& ra, size_t lds, hipStream_t s) {
-  auto kern = route_kernel<Tin, NOISY, TN, TM>;
-  hipLaunchKernelGGL(kern, dim3(ra.nblk), dim3(256), lds, s, ra);
+  hipLaunchKernelGGL((route_kernel<Tin, NOISY, EPW>), dim3(ra.nblk), dim3(64 * ra.nw), lds, s, ra);
   return hipGetLastError();
 }
 
 template <typename Tin, bool NOISY>
-hipError_t dispatch_route_shape(int tn, int tm, const RouteArgs& ra, size_t lds, hipStream_t s) {
-  if (tn == 1 && tm == 8) return launch_route_t<Tin, NOISY, 1, 8>(ra, lds, s);
-  if (tn == 1 && tm == 4) return launch_route_t<Tin, NOISY, 1, 4>(ra, lds, s);
-  if (tn == 2 && tm == 8) return launch_route_t<Tin, NOISY, 2, 8>(ra, lds, s);
-  if (tn == 2 && tm == 4) return launch_route_t<Tin, NOISY, 2, 4>(ra, lds, s);
-  if (tn == 4 && tm == 4) return launch_route_t<Tin, NOISY, 4, 4>(ra, lds, s);
-  if (tn == 4 && tm == 2) return launch_route_t<Tin, NOISY, 4, 2>(ra, lds, s);
-  if (tn == 8 && tm == 2) return launch_route_t<Tin, NOISY, 8, 2>(ra, lds, s);
-  if (tn == 8 && tm == 1) return launch_route_t<Tin, NOISY, 8, 1>(ra, lds, s);
-  if (tn == 16 && tm == 1) return launch_route_t<Tin, NOISY, 16, 1>(ra, lds, s);
-  return hipErrorInvalidValue;
+hipError_t launch_route_epw(int epw, const RouteArgs& ra, size_t lds, hipStream_t s) {
+  if (epw == 16) return launch_route_t<Tin, NOISY, 16>(ra, lds, s);
+  if (epw == 32) return launch_route_t<Tin, NOISY, 32>(ra, lds, s);
+  return launch_route_t<Tin, NOISY, 64>(ra, lds, s);
 }
 
 }  // namespace
 }  // namespace moe
 
-int route_tokens_per_block(int E, bool noisy) {
-  int tn, tm;
-  moe::route_shape(E, noisy, &tn, &tm);
-  return 4 * tm;
+int route_tokens_per_block(int E, bool noisy) { return 64; }
+
+size_t route_weight_floats(int d, int E) {
+  const int epw = moe::route_epw(E);
+  const int epad = ((E + epw - 1) / epw) * epw;
+  return (size_t)d * epad;
 }
 
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
   using namespace moe;
   const bool noisy = a.w_noise != nullptr;
-  int tn, tm;
-  route_shape(a.E, noisy, &tn, &tm);
-  const int ep = 64 * tn;
-  const int tpb = 4 * tm;
-  const int nblk = (int)((a.T + tpb - 1) / tpb);
-  int bk = 16384 / (ep * (noisy ? 2 : 1));
-  bk = bk > 64 ? 64 : bk;
-  bk = (bk / 8) * 8;
-  if (bk < 8) bk = 8;
+  const int epw = route_epw(a.E);
+  const int nw = (a.E + epw - 1) / epw;
+  const int epad = nw * epw;
+  const int nblk = (int)((a.T + 63) / 64);
   hipError_t err = hipSuccess;
   if (a.T > 0) {
+    const int64_t nw32 = (int64_t)a.d * epad;
+    const dim3 pg((unsigned)((nw32 + 255) / 256));
+    if (a.dtype == 1) {
+      hipLaunchKernelGGL(route_prep_kernel<uint16_t>, pg, dim3(256), 0, s, static_cast<const uint16_t*>(a.w_gate),
+                         a.w32, a.d, a.E, epad);
+      if (noisy)
+        hipLaunchKernelGGL(route_prep_kernel<uint16_t>, pg, dim3(256), 0, s,
+                           static_cast<const uint16_t*>(a.w_noise), a.wn32, a.d, a.E, epad);
+    } else {
+      hipLaunchKernelGGL(route_prep_kernel<float>, pg, dim3(256), 0, s, static_cast<const float*>(a.w_gate), a.w32,
+                         a.d, a.E, epad);
+      if (noisy)
+        hipLaunchKernelGGL(route_prep_kernel<float>, pg, dim3(256), 0, s, static_cast<const float*>(a.w_noise),
+                           a.wn32, a.d, a.E, epad);
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     RouteArgs ra;
     ra.T = a.T;
     ra.d = a.d;
     ra.E = a.E;
+    ra.epad = epad;
     ra.k = a.k;
     ra.kk = noisy ? (a.k + 1 < a.E ? a.k + 1 : a.E) : a.k;
     ra.renormalize = a.renormalize;
-    ra.bk = bk;
     ra.nblk = nblk;
+    ra.nw = nw;
     ra.x = a.x;
-    ra.w_gate = a.w_gate;
+    ra.w32 = a.w32;
+    ra.wn32 = noisy ? a.wn32 : nullptr;
     ra.gate_bias = a.gate_bias;
-    ra.w_noise = a.w_noise;
     ra.noise = a.noise;
     ra.topk_idx = a.topk_idx;
     ra.topk_gate = a.topk_gate;
@@ -531,15 +534,11 @@ hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
     ra.part_imp = a.part_imp;
     ra.part_load = a.part_load;
     ra.part_cnt = a.part_cnt;
-    size_t stage = (size_t)bk * ep * (noisy ? 2 : 1);
-    size_t redn = (size_t)16 * ep;
-    size_t lds = 4 * (stage > redn ? stage : redn);
+    const size_t lds = sizeof(float) * ((size_t)2 * nw * ra.kk * 64 + 2 * nw * 64 + 21 * 64);
     if (a.dtype == 1) {
-      err = noisy ? dispatch_route_shape<uint16_t, true>(tn, tm, ra, lds, s)
-                  : dispatch_route_shape<uint16_t, false>(tn, tm, ra, lds, s);
+      err = noisy ? launch_route_epw<uint16_t, true>(epw, ra, lds, s) : launch_route_epw<uint16_t, false>(epw, ra, lds, s);
     } else {
-      err = noisy ? dispatch_route_shape<float, true>(tn, tm, ra, lds, s)
-                  : dispatch_route_shape<float, false>(tn, tm, ra, lds, s);
+      err = noisy ? launch_route_epw<float, true>(epw, ra, lds, s) : launch_route_epw<float, false>(epw, ra, lds, s);
     }
     if (err != hipSuccess) return err;
   }
