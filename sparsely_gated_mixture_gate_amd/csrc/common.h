@@ -32,6 +32,31 @@ __device__ __forceinline__ float activation(float z) {
   }
 }
 
+// GELU for bf16 outputs: erf from Abramowitz & Stegun 7.1.26 (absolute error
+// <= 1.5e-7, far below bf16 rounding), branch-free, with one reciprocal and one
+// exp2. With a = |z|/sqrt 2 and q = P(t) t exp(-a^2), t = 1/(1 + p a),
+// erf(a) = 1 - q, so 1 + erf(z/sqrt 2) = 2 - q for z >= 0 and q for z < 0 (no
+// cancellation for negative z).
+__device__ __forceinline__ float gelu_fast(float z) {
+  const float a = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
+  float p = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  p = __builtin_fmaf(p, t, 1.421413741f);
+  p = __builtin_fmaf(p, t, -0.284496736f);
+  p = __builtin_fmaf(p, t, 0.254829592f);
+  const float q = p * t * __builtin_amdgcn_exp2f(-(a * a) * 1.4426950408889634f);
+  return 0.5f * z * (z >= 0.0f ? 2.0f - q : q);
+}
+
+template <int ACT>
+__device__ __forceinline__ float activation_bf16(float z) {
+  if constexpr (ACT == 0) {
+    return z > 0.0f ? z : 0.0f;
+  } else {
+    return gelu_fast(z);
+  }
+}
+
 }  // namespace moe
 
 // ---------------------------------------------------------------------------

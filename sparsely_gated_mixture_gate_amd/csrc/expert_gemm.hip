@@ -23,8 +23,8 @@
 //     ds_read_b64_tr_b16 (two per operand). Double-buffered LDS with the next
 //     tiles' global loads in flight (register staging two k-tiles ahead). The MFMA runs with swapped
 //     operands (D = W^T A^T) so each lane ends with 4 consecutive output columns
-//     of a row (8-byte stores); ReLU / exact GELU is applied in fp32 before the
-//     bf16 (nearest-even) store.
+//     of a row (8-byte stores); ReLU / GELU is applied in fp32 before the bf16
+//     (nearest-even) store, GELU with a branch-free erf accurate to 1.5e-7.
 //   * scheduling: real tiles are dealt evenly to the 8 XCDs in contiguous
 //     chunks (tiles sharing an activation or weight panel share that XCD's L2),
 //     rastered inside each expert in groups of 4 M-tiles.
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
       if (gcol >= N) continue;
       float v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = APPLY_ACT ? activation<ACT>(acc[mi][ni][j]) : acc[mi][ni][j];
+      for (int j = 0; j < 4; ++j) v[j] = APPLY_ACT ? activation_bf16<ACT>(acc[mi][ni][j]) : acc[mi][ni][j];
       uint2 o;
       o.x = pack_bf16x2(v[0], v[1]);
       o.y = pack_bf16x2(v[2], v[3]);
