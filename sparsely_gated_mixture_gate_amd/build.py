@@ -18,6 +18,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
@@ -55,7 +56,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, os.path.basename(src).replace(".hip", ".o"))
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

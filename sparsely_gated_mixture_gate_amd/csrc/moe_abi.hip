@@ -8,7 +8,7 @@
 
 #include <string>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "common.h"
 
 hipError_t launch_softplus(const float* z, float* out, int64_t n, hipStream_t s);
