@@ -76,8 +76,8 @@ struct RouteLaunch {
   float* aux_out;
   float* logits_out;
   // workspace pieces
-  float* w32;        // [d][epad] fp32 gate weights
-  float* wn32;       // [d][epad] fp32 noise weights (noisy gate)
+  float* wc;         // [d][ncol] fp32 gate (and noise) weights in column blocks
+  float* lg;         // route_logit_floats(T, E, noisy): logits H [, clean logits, softplus of noise logits]
   float* part_prob;  // [E][nblk]
   float* part_imp;   // [E][nblk]
   float* part_load;  // [E][nblk]
@@ -85,7 +85,8 @@ struct RouteLaunch {
   double* red;       // [3][E]
 };
 int route_tokens_per_block(int E, bool noisy);
-size_t route_weight_floats(int d, int E);
+size_t route_weight_floats(int d, int E, bool noisy);
+size_t route_logit_floats(int64_t T, int E, bool noisy);
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
 
 struct DispatchLaunch {

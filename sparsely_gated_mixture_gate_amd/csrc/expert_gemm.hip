@@ -30,6 +30,7 @@
 //     rastered inside each expert in groups of 4 M-tiles.
 //   * fp32 path: a plain LDS-tiled fp32 FMA kernel (64x64x16 tiles).
 #include "common.h"
+#include "lds_dma.h"
 
 namespace moe {
 namespace {
@@ -116,61 +117,6 @@ __device__ __forceinline__ bool schedule_tile(const int32_t* __restrict__ tile_s
   return true;
 }
 
-typedef int int32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource for a raw byte range (stride 0, 32-bit data format); loads at
-// offsets >= num_bytes return zero.
-__device__ __forceinline__ int32x4 buffer_rsrc(const void* base, uint32_t num_bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  int32x4 r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)(uint32_t)((a >> 32) & 0xFFFFu);
-  r[2] = (int)num_bytes;
-  r[3] = 0x00020000;
-  return r;
-}
-
-// Asynchronous 16-byte load straight into LDS: lane l of the wave writes bytes
-// lds_base + 16*l .. +15. The load counts in vmcnt; it writes no VGPR, so nothing
-// in registers can be clobbered while it is in flight.
-__device__ __forceinline__ void load_to_lds(uint32_t lds_base, int voffset, const int32x4& rsrc, int soffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
-               : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N) (expcnt / lgkmcnt not waited).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-
-// Wait until at most rem * LD of this thread's loads are in flight (rem = k-tiles
-// issued after the one about to be read).
-template <int LD, int MAXREM>
-__device__ __forceinline__ void wait_tiles(int rem) {
-  if constexpr (MAXREM >= 3) {
-    if (rem >= 3) { wait_vmcnt<3 * LD>(); return; }
-  }
-  if constexpr (MAXREM >= 2) {
-    if (rem >= 2) { wait_vmcnt<2 * LD>(); return; }
-  }
-  if constexpr (MAXREM >= 1) {
-    if (rem >= 1) { wait_vmcnt<LD>(); return; }
-  }
-  wait_vmcnt<0>();
-}
-
-// Barrier without a memory fence (a fence would drain the in-flight prefetches);
-// the empty asm statements keep the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <int RC>
 __device__ __forceinline__ int swz_a_rc(int row) {
   if constexpr (RC == 8) {
@@ -244,8 +190,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
     voffB[i] = gn < N ? (kr * N + gn) * 2 : kOut;
     voffB_last[i] = (gn < N && k_last + kr < K) ? (kr * N + gn) * 2 : kOut;
   }
-  typedef __attribute__((address_space(3))) uint4 lds_uint4;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_uint4*)(&smem[0]);
+  const uint32_t lds0 = lds_address(&smem[0]);
 
   auto issue = [&](int kt) {
     const int st = kt % NSTAGE;

@@ -59,6 +59,9 @@ moe_status check_params(const moe_params* p) {
   if ((int64_t)p->d_model * p->d_ff * elt >= (int64_t(1) << 31) - 16 ||
       p->T * (int64_t)p->k * widest * elt >= (int64_t(1) << 32))
     return fail(MOE_ERR_UNSUPPORTED, "an expert's weights or the permuted rows exceed 32-bit byte offsets");
+  // 32-bit byte offsets inside the fp32 gate (+ noise) weights, column blocks of 128
+  if ((int64_t)p->d_model * (2 * ((p->E + 63) / 64) * 64 + 128) * 4 >= (int64_t(1) << 31) - 16)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model * E too large for the gate weights' 32-bit byte offsets");
   return MOE_OK;
 }
 
@@ -93,7 +96,7 @@ struct Carver {
 };
 
 struct RouteWs {
-  float *w32, *wn32;
+  float *wc, *lg;
   float *part_prob, *part_imp, *part_load;
   int32_t* part_cnt;
   double* red;
@@ -103,8 +106,8 @@ RouteWs carve_route(Carver& c, const moe_params* p, bool noisy) {
   const int64_t nblk = (p->T + tpb - 1) / tpb;
   const size_t n = (size_t)p->E * (size_t)(nblk > 0 ? nblk : 1);
   RouteWs w;
-  w.w32 = c.take<float>(route_weight_floats(p->d_model, p->E));
-  w.wn32 = noisy ? c.take<float>(route_weight_floats(p->d_model, p->E)) : nullptr;
+  w.wc = c.take<float>(route_weight_floats(p->d_model, p->E, noisy));
+  w.lg = c.take<float>(route_logit_floats(p->T, p->E, noisy));
   w.part_prob = c.take<float>(n);
   w.part_imp = c.take<float>(n);
   w.part_load = c.take<float>(n);
@@ -214,8 +217,8 @@ moe_status run_route(const moe_params* p, const void* x, const void* w_gate, con
   a.counts_routed = counts_routed;
   a.aux_out = aux_out;
   a.logits_out = logits_out;
-  a.w32 = w.w32;
-  a.wn32 = w.wn32;
+  a.wc = w.wc;
+  a.lg = w.lg;
   a.part_prob = w.part_prob;
   a.part_imp = w.part_imp;
   a.part_load = w.part_load;

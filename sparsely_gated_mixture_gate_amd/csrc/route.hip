@@ -11,22 +11,28 @@
 //
 // Design (gfx950): the gate GEMM is fp32 FMA in a fixed order -- each logit
 // accumulates x[t,j] * W[j,e] from +0 for j ascending, one fma per term -- so
-// the integer routing is reproducible bit-for-bit. A block holds 64 tokens, one
-// per lane, and E/EPW waves; wave w owns experts [w*EPW, (w+1)*EPW). A small
-// prep kernel widens W_gate (and W_noise) to fp32 once per call; inside the
-// loop each weight row slice is wave-uniform, arrives by scalar loads and is the
-// scalar operand of v_fmac_f32, while each lane's x row arrives by 16-byte
-// vector loads (bf16 widened once per value). Each wave then keeps its top-(k+1)
-// candidates and softmax statistics (max, sum of exp) per token in LDS; one wave
-// merges them (candidates by value descending, expert index ascending; sums
-// rescaled to the common max in wave order) into the top-k, the gates and the
-// thresholds of the load estimator; every wave then reduces its experts'
-// probabilities, gates, counts and load estimates over the 64 tokens with
-// butterfly shuffles. Per-block partial sums go to the workspace and are reduced
-// in a fixed order by route_reduce / route_aux (deterministic, no float atomics).
+// the integer routing is reproducible bit-for-bit. Steps:
+//   * route_prep widens W_gate (and W_noise) to fp32 once per call, laid out in
+//     column blocks of BN (a noisy block holds BN/2 experts' gate columns and the
+//     same experts' noise columns);
+//   * route_logits is a register-blocked fp32 FMA GEMM: a block computes 64
+//     tokens x BN columns, each thread 4 tokens x 8 columns, with both operands
+//     streamed into a 4-stage LDS ring by direct-to-LDS buffer loads (x in its
+//     storage type, widened once per value in registers). Its epilogue adds the
+//     bias and, for the noisy gate, forms Softplus and H, writing H (and the clean
+//     logits and Softplus values the load estimator needs) to the workspace;
+//   * route_select holds 64 tokens: lane = token, each wave scans 64 experts for
+//     its top-(k+1) candidates and softmax statistics; one wave merges them
+//     (candidates by value descending, expert index ascending; sums rescaled to
+//     the common max in wave order) into the top-k, the gates and the thresholds
+//     of the load estimator; then lane = expert, each lane sums its expert's
+//     probability, gate, count and load estimate over the 64 tokens in order.
+// Per-block partial sums go to the workspace and are reduced in a fixed order by
+// route_reduce / route_aux (deterministic, no float atomics).
 #include <float.h>
 
 #include "common.h"
+#include "lds_dma.h"
 
 namespace moe {
 namespace {
@@ -89,10 +95,10 @@ __device__ __forceinline__ bool better(float v, int e, float bv, int be) { retur
 
 struct RouteArgs {
   int64_t T;
-  int d, E, epad, k, kk, renormalize, nblk, nw;
-  const void* x;
-  const float* w32;   // [d][epad] fp32 copy of W_gate (zero columns past E)
-  const float* wn32;  // [d][epad] fp32 copy of W_noise, or null
+  int E, lpad, k, renormalize, nblk, epw;
+  const float* H;     // [T][lpad] logits H (noisy: clean + eps * softplus)
+  const float* CL;    // [T][lpad] clean logits x W_gate (+ b), noisy gate only
+  const float* SG;    // [T][lpad] Softplus(x W_noise), noisy gate only
   const float* gate_bias;
   const float* noise;
   int32_t* topk_idx;
@@ -104,177 +110,349 @@ struct RouteArgs {
   int32_t* part_cnt;
 };
 
+// fp32 gate weights in column blocks of BN: wc[j][q*BN + c]. Gate only: column
+// c of block q is expert q*BN + c. Noisy: block q covers experts q*BN/2 .. +BN/2,
+// columns c < BN/2 from W_gate and c >= BN/2 from W_noise. Zero past E.
 template <typename Tin>
-__global__ __launch_bounds__(256) void route_prep_kernel(const Tin* __restrict__ w, float* __restrict__ w32,
-                                                         int d, int E, int epad) {
+__global__ __launch_bounds__(256) void route_prep_kernel(const Tin* __restrict__ w_gate,
+                                                         const Tin* __restrict__ w_noise, float* __restrict__ wc,
+                                                         int d, int E, int ncol, int bn) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)d * epad) return;
-  const int64_t j = i / epad;
-  const int e = (int)(i - j * epad);
+  if (i >= (int64_t)d * ncol) return;
+  const int64_t j = i / ncol;
+  const int col = (int)(i - j * ncol);
+  const int q = col / bn, c = col - q * bn;
+  const Tin* src = w_gate;
+  int e = q * bn + c;
+  if (w_noise) {
+    const int half = bn / 2;
+    e = q * half + (c < half ? c : c - half);
+    if (c >= half) src = w_noise;
+  }
   float v = 0.0f;
   if (e < E) {
     if constexpr (sizeof(Tin) == 2) {
-      v = bf16_to_f32(w[j * E + e]);
+      v = bf16_to_f32(src[j * E + e]);
     } else {
-      v = w[j * E + e];
+      v = src[j * E + e];
     }
   }
-  w32[i] = v;
+  wc[i] = v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+constexpr int kLgTok = 64;    // tokens per logits block
+constexpr int kLgJC = 32;     // j values per LDS stage
+constexpr int kLgStages = 4;  // LDS ring depth
+
+// Raw gate (and noise) accumulators for 64 tokens x one column block of BN:
+// acc[t][c] = fma chain over j ascending of x[t][j] * wc[j][q*BN + c], from +0.
+// Thread (tq, eg) of 16 x BN/8 owns tokens tq + 16 i (i < 4) and columns
+// 4 eg .. +3 and BN/2 + 4 eg .. +3, so a wave's LDS reads of one weight row
+// touch consecutive 16-byte chunks and its x reads 4 (8) consecutive rows,
+// whose chunks are XOR-swizzled apart.
+template <typename Tin, int BN>
+__global__ __launch_bounds__(2 * BN) void route_logits_kernel(const Tin* __restrict__ x,
+                                                              const float* __restrict__ wc, int64_t T, int d,
+                                                              int E, int ncol, int lpad, int noisy,
+                                                              const float* __restrict__ bias,
+                                                              const float* __restrict__ noise, float* __restrict__ H,
+                                                              float* __restrict__ CL, float* __restrict__ SG) {
+  constexpr int NT = 2 * BN;
+  constexpr int EG = BN / 8;
+  constexpr int SZ = sizeof(Tin);
+  constexpr int CPR = kLgJC * SZ / 16;      // 16-byte chunks of an x row per stage
+  constexpr int SWM = (CPR < 8 ? CPR : 8) - 1;
+  constexpr int X_CH = kLgTok * CPR;
+  constexpr int WCR = BN / 4;               // 16-byte chunks of a weight row
+  constexpr int W_CH = kLgJC * WCR;
+  constexpr int X_LD = X_CH / NT, W_LD = W_CH / NT, LD = X_LD + W_LD;
+  constexpr int STAGE_CH = X_CH + W_CH;
+  static_assert(X_CH % NT == 0 && W_CH % NT == 0, "stage / thread mismatch");
+  __shared__ uint4 smem[kLgStages * STAGE_CH];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int eg = tid % EG, tq = tid / EG;
+  const int64_t t0 = (int64_t)blockIdx.x * kLgTok;
+  const int q = blockIdx.y;
+  const int rows = (int)min<int64_t>(kLgTok, T - t0);
+  const int nk = (d + kLgJC - 1) / kLgJC;
+
+  // x rows past T are clamped (read, never stored); chunks past d in the last
+  // stage are loaded but never read, weight rows past d load zero. The stage
+  // offset goes into the per-lane offset, so the whole offset is range-checked
+  // against the buffer size.
+  const int32x4 rsX = buffer_rsrc(x + t0 * d, (uint32_t)rows * d * SZ);
+  const int32x4 rsW = buffer_rsrc(wc + q * BN, (uint32_t)((int64_t)d * ncol - q * BN) * 4);
+  int voffX[X_LD], voffW[W_LD];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;  // identical on every lane: each butterfly step adds the same two values
+  for (int i = 0; i < X_LD; ++i) {
+    const int sl = tid + NT * i;
+    const int r = sl / CPR, p = sl % CPR;
+    voffX[i] = min(r, rows - 1) * d * SZ + (p ^ (r & SWM)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < W_LD; ++i) {
+    const int sl = tid + NT * i;
+    voffW[i] = (sl / WCR) * ncol * 4 + (sl % WCR) * 16;
+  }
+  const uint32_t lds0 = lds_address(&smem[0]);
+  auto issue = [&](int kt) {
+    const int st = kt % kLgStages;
+#pragma unroll
+    for (int i = 0; i < X_LD; ++i)
+      load_to_lds(__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((st * STAGE_CH + i * NT + wave * 64) * 16)),
+                  voffX[i] + kt * kLgJC * SZ, rsX, 0);
+#pragma unroll
+    for (int i = 0; i < W_LD; ++i)
+      load_to_lds(
+          __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((st * STAGE_CH + X_CH + i * NT + wave * 64) * 16)),
+          voffW[i] + kt * kLgJC * ncol * 4, rsW, 0);
+  };
+
+  float acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[i][c] = 0.0f;
+
+  // One step = 8 j values: the thread's 4 x chunks (8 values of each token)
+  // and 8 x 2 weight chunks, consumed in two halves of 4 j. The LDS reads of
+  // half h+1 are issued before the fmas of half h (two register sets; at most
+  // 12 reads in flight, within the lgkmcnt range).
+  typedef uint4 XRegs[4][SZ / 2];
+  typedef float4 WRegs[4][2];
+  auto load_x = [&](int st, int step, XRegs& xr) {
+    const uint4* sx = &smem[st * STAGE_CH];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = tq + 16 * i;
+#pragma unroll
+      for (int h = 0; h < SZ / 2; ++h) xr[i][h] = sx[r * CPR + (((SZ / 2) * step + h) ^ (r & SWM))];
+    }
+  };
+  auto load_w = [&](int st, int half, WRegs& w) {
+    const float4* sw = reinterpret_cast<const float4*>(&smem[st * STAGE_CH + X_CH]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      w[u][0] = sw[(half * 4 + u) * WCR + eg];
+      w[u][1] = sw[(half * 4 + u) * WCR + EG + eg];
+    }
+  };
+  float xv[4][8];
+  auto unpack_x = [&](const XRegs& xr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (SZ == 2) {
+        const uint4 v = xr[i][0];
+        xv[i][0] = bf16_lo(v.x); xv[i][1] = bf16_hi(v.x);
+        xv[i][2] = bf16_lo(v.y); xv[i][3] = bf16_hi(v.y);
+        xv[i][4] = bf16_lo(v.z); xv[i][5] = bf16_hi(v.z);
+        xv[i][6] = bf16_lo(v.w); xv[i][7] = bf16_hi(v.w);
+      } else {
+        const uint4 v0 = xr[i][0], v1 = xr[i][SZ / 2 - 1];
+        xv[i][0] = __uint_as_float(v0.x); xv[i][1] = __uint_as_float(v0.y);
+        xv[i][2] = __uint_as_float(v0.z); xv[i][3] = __uint_as_float(v0.w);
+        xv[i][4] = __uint_as_float(v1.x); xv[i][5] = __uint_as_float(v1.y);
+        xv[i][6] = __uint_as_float(v1.z); xv[i][7] = __uint_as_float(v1.w);
+      }
+    }
+  };
+  auto fma_half = [&](int ub, const WRegs& w) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wv[8] = {w[u][0].x, w[u][0].y, w[u][0].z, w[u][0].w, w[u][1].x, w[u][1].y, w[u][1].z, w[u][1].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[i][c] = __builtin_fmaf(xv[i][ub + u], wv[c], acc[i][c]);
+    }
+  };
+  XRegs xs[2];
+  WRegs ws[2];
+  auto compute = [&](int st, int nsteps) {
+    const int nh = 2 * nsteps;
+    load_x(st, 0, xs[0]);
+    load_w(st, 0, ws[0]);
+#pragma unroll
+    for (int h = 0; h < kLgJC / 4; ++h) {
+      if (h >= nh) break;
+      if (h + 1 < nh) {
+        if (((h + 1) & 1) == 0) load_x(st, (h + 1) / 2, xs[((h + 1) / 2) & 1]);
+        load_w(st, h + 1, ws[(h + 1) & 1]);
+      }
+      if ((h & 1) == 0) unpack_x(xs[(h / 2) & 1]);
+      fma_half(4 * (h & 1), ws[h & 1]);
+    }
+  };
+
+#pragma unroll
+  for (int t = 0; t < kLgStages - 1; ++t)
+    if (t < nk) issue(t);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_tiles<LD, kLgStages - 2>(min(kLgStages - 2, nk - 1 - kt));
+    block_barrier();  // stage kt is in LDS for every wave; the buffer of stage kt-1 is free
+    if (kt + kLgStages - 1 < nk) issue(kt + kLgStages - 1);
+    compute(kt % kLgStages, min(kLgJC, d - kt * kLgJC) / 8);
+  }
+
+  // Epilogue: logits of the thread's 4 tokens x 4 experts (x 2 for the gate-only
+  // layout). Clean logit = acc + bias (one rounding); noisy: softplus of the noise
+  // accumulator and H = fma(eps, softplus, clean).
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + tq + 16 * i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (noisy && half == 1) break;
+      const int e = noisy ? q * (BN / 2) + 4 * eg : q * BN + half * (BN / 2) + 4 * eg;
+      if (e >= lpad) continue;
+      float cv[4], sg[4], hv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool valid = e + c < E;
+        cv[c] = acc[i][4 * half + c];
+        if (bias && valid) cv[c] = cv[c] + bias[e + c];
+        hv[c] = cv[c];
+        if (noisy) {
+          sg[c] = canon_softplus(acc[i][4 + c]);
+          if (valid) hv[c] = __builtin_fmaf(noise[t * E + e + c], sg[c], cv[c]);
+        }
+      }
+      *reinterpret_cast<float4*>(H + t * lpad + e) = float4{hv[0], hv[1], hv[2], hv[3]};
+      if (noisy) {
+        *reinterpret_cast<float4*>(CL + t * lpad + e) = float4{cv[0], cv[1], cv[2], cv[3]};
+        *reinterpret_cast<float4*>(SG + t * lpad + e) = float4{sg[0], sg[1], sg[2], sg[3]};
+      }
+    }
+  }
 }
 
-// One block = 64 tokens (one per lane) x all experts; wave w owns experts
-// [w*EPW, (w+1)*EPW). Each lane accumulates its token's logits for the wave's
-// experts as fixed ascending-j fma chains: x arrives per lane (16-byte vector
-// loads, unpacked once) and the fp32 weight row W[j][e0 .. e0+EPW) is
-// wave-uniform, read with scalar loads and used as the scalar FMA operand.
-template <typename Tin, bool NOISY, int EPW>
-__global__ __launch_bounds__(1024) void route_kernel(RouteArgs a) {
+// Per-token routing and per-expert partial sums for a block of 64 tokens and
+// 16 waves.
+//  1. lane = token: wave w scans experts [w*epw, (w+1)*epw), keeping the
+//     top-KK (value descending, index ascending) and the softmax statistics
+//     (max, then sum of exp) of its range;
+//  2. wave 0 merges the 16 sorted candidate lists (sums rescaled to the common
+//     max in wave order) into the top-k, the gates and the thresholds of the
+//     load estimator, and writes the token's results;
+//  3. lane = expert: wave w takes expert group w % G (G = ceil(E/64)) and token
+//     slice w / G of 16/G slices, accumulating each expert's softmax
+//     probability, gate, count and load estimate over its slice in token order;
+//     the slices are then added in slice order.
+template <bool NOISY, int KK>
+__global__ __launch_bounds__(1024) void route_select_kernel(RouteArgs a) {
   extern __shared__ float smem[];
-  const Tin* __restrict__ x = static_cast<const Tin*>(a.x);
-  const float* __restrict__ w32 = a.w32;
-  const float* __restrict__ wn32 = a.wn32;
-  const int d = a.d, E = a.E, k = a.k, kk = a.kk, nw = a.nw, epad = a.epad;
+  constexpr int NW = 16;
+  constexpr int KS = KK < 8 ? KK : 8;  // selectable slots (k <= KS)
+  constexpr int RS = 24;  // floats per token in res: m, S, thr_out, thr_in, sel[8], gate[8], pad
+  const int E = a.E, k = a.k, lpad = a.lpad, epw = a.epw;
   const int64_t T = a.T;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int e0 = wave * EPW;
-  const int64_t t = (int64_t)blockIdx.x * 64 + lane;
-  const bool tok_ok = t < T;
-  const Tin* __restrict__ xrow = x + (tok_ok ? t : T - 1) * d;  // rows past T: computed, never stored
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int nt = (int)min<int64_t>(64, T - t0);
+  float* cand_v = smem;                                        // [NW][KK][64]
+  int* cand_i = reinterpret_cast<int*>(smem + NW * KK * 64);   // [NW][KK][64]
+  float* wmax = smem + 2 * NW * KK * 64;                       // [NW][64]
+  float* wsum = wmax + NW * 64;                                // [NW][64]
+  float* res = wsum + NW * 64;                                 // [64][RS]
+  float* part = res + 64 * RS;                                 // [4][NW*64]: slice partials
 
-  float acc[EPW], accn[EPW];
-#pragma unroll
-  for (int c = 0; c < EPW; ++c) acc[c] = accn[c] = 0.0f;
-
-  // x chunks are prefetched one 8-wide step ahead
-  constexpr int XW = sizeof(Tin) == 2 ? 1 : 2;  // 16-byte words per 8 values
-  uint4 xn[XW];
-#pragma unroll
-  for (int q = 0; q < XW; ++q) xn[q] = reinterpret_cast<const uint4*>(xrow)[q];
-  for (int j = 0; j < d; j += 8) {
-    uint4 xc[XW];
-#pragma unroll
-    for (int q = 0; q < XW; ++q) xc[q] = xn[q];
-    if (j + 8 < d) {
-#pragma unroll
-      for (int q = 0; q < XW; ++q) xn[q] = reinterpret_cast<const uint4*>(xrow + j + 8)[q];
-    }
-    float xv[8];
-    if constexpr (sizeof(Tin) == 2) {
-      xv[0] = bf16_lo(xc[0].x); xv[1] = bf16_hi(xc[0].x);
-      xv[2] = bf16_lo(xc[0].y); xv[3] = bf16_hi(xc[0].y);
-      xv[4] = bf16_lo(xc[0].z); xv[5] = bf16_hi(xc[0].z);
-      xv[6] = bf16_lo(xc[0].w); xv[7] = bf16_hi(xc[0].w);
-    } else {
-      xv[0] = __uint_as_float(xc[0].x); xv[1] = __uint_as_float(xc[0].y);
-      xv[2] = __uint_as_float(xc[0].z); xv[3] = __uint_as_float(xc[0].w);
-      xv[4] = __uint_as_float(xc[XW - 1].x); xv[5] = __uint_as_float(xc[XW - 1].y);
-      xv[6] = __uint_as_float(xc[XW - 1].z); xv[7] = __uint_as_float(xc[XW - 1].w);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float* __restrict__ wrow = w32 + (int64_t)(j + u) * epad + e0;
-#pragma unroll
-      for (int c = 0; c < EPW; ++c) acc[c] = __builtin_fmaf(xv[u], wrow[c], acc[c]);
-      if constexpr (NOISY) {
-        const float* __restrict__ nrow = wn32 + (int64_t)(j + u) * epad + e0;
-#pragma unroll
-        for (int c = 0; c < EPW; ++c) accn[c] = __builtin_fmaf(xv[u], nrow[c], accn[c]);
-      }
-    }
-  }
-
-  // ---- logits of this wave's experts ----------------------------------------
-  float h[EPW], cl[EPW], sg[EPW];
-#pragma unroll
-  for (int c = 0; c < EPW; ++c) {
-    const int e = e0 + c;
-    const bool valid = e < E;
-    float cv = acc[c];
-    if (a.gate_bias && valid) cv = cv + a.gate_bias[e];
-    cl[c] = cv;
-    if constexpr (NOISY) {
-      sg[c] = canon_softplus(accn[c]);
-      h[c] = valid ? __builtin_fmaf(a.noise[(tok_ok ? t : T - 1) * E + e], sg[c], cv) : -INFINITY;
-    } else {
-      sg[c] = 1.0f;
-      h[c] = valid ? cv : -INFINITY;
-    }
-    if (a.logits_out && valid && tok_ok) a.logits_out[t * E + e] = h[c];
-  }
-
-  // ---- wave-local top-kk candidates and softmax statistics -------------------
-  // LDS: cand_v/cand_i [nw][kk][64], wmax/wsum [nw][64], results per token.
-  float* cand_v = smem;
-  int* cand_i = reinterpret_cast<int*>(smem + nw * kk * 64);
-  float* wmax = smem + 2 * nw * kk * 64;
-  float* wsum = wmax + nw * 64;
-  float* res = wsum + nw * 64;  // [5 + 2*8][64]: m, 1/S, thr_out, thr_in, have_in, sel[8], gate[8]
+  // ---- 1. lane = token: candidates and softmax statistics of this wave's range
   {
-    uint64_t taken = 0;
-    float m_w = -INFINITY;
+    const int e_lo = min(E, wave * epw), e_hi = min(E, e_lo + epw);
+    const int64_t t = t0 + lane;
+    const float* hrow = a.H + (t < T ? t : T - 1) * lpad;  // rows past T: computed, never stored
+    float bv[KK];
+    int bi[KK];
 #pragma unroll
-    for (int r = 0; r < 9; ++r) {
-      if (r >= kk) break;
-      float best = -INFINITY;
-      int bi = -1;
+    for (int r = 0; r < KK; ++r) {
+      bv[r] = -INFINITY;
+      bi[r] = 0x7FFFFFFF;
+    }
+    for (int e0 = e_lo; e0 < e_hi; e0 += 16) {
+      float hv[16];  // all four loads in flight together
 #pragma unroll
-      for (int c = 0; c < EPW; ++c) {
-        if (e0 + c < E && !((taken >> c) & 1ull) && (bi < 0 || h[c] > best)) {  // strict '>': lower index on ties
-          best = h[c];
-          bi = c;
+      for (int c = 0; c < 16; c += 4) {
+        float4 h4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (e0 + c < e_hi) h4 = *reinterpret_cast<const float4*>(hrow + e0 + c);
+        hv[c] = h4.x; hv[c + 1] = h4.y; hv[c + 2] = h4.z; hv[c + 3] = h4.w;
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        float v = hv[c];
+        int i = e0 + c;
+        if (i >= e_hi) break;
+        if (!better(v, i, bv[KK - 1], bi[KK - 1])) continue;
+#pragma unroll
+        for (int r = 0; r < KK; ++r) {
+          if (better(v, i, bv[r], bi[r])) {
+            const float tv = bv[r];
+            const int ti = bi[r];
+            bv[r] = v;
+            bi[r] = i;
+            v = tv;
+            i = ti;
+          }
         }
       }
-      if (bi >= 0) taken |= 1ull << bi;
-      if (r == 0) m_w = best;
-      cand_v[(wave * kk + r) * 64 + lane] = best;
-      cand_i[(wave * kk + r) * 64 + lane] = bi >= 0 ? e0 + bi : 0x7FFFFFFF;
     }
+    const float m_w = bv[0];
     float s_w = 0.0f;
+    for (int e0 = e_lo; e0 < e_hi; e0 += 16) {
+      float hv[16];
 #pragma unroll
-    for (int c = 0; c < EPW; ++c)
-      if (e0 + c < E) s_w += expf(h[c] - m_w);
-    wmax[wave * 64 + lane] = m_w;
+      for (int c = 0; c < 16; c += 4) {
+        float4 h4 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (e0 + c < e_hi) h4 = *reinterpret_cast<const float4*>(hrow + e0 + c);
+        hv[c] = h4.x; hv[c + 1] = h4.y; hv[c + 2] = h4.z; hv[c + 3] = h4.w;
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        if (e0 + c < e_hi) s_w += expf(hv[c] - m_w);
+    }
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
+      cand_v[(wave * KK + r) * 64 + lane] = bv[r];
+      cand_i[(wave * KK + r) * 64 + lane] = bi[r];
+    }
+    wmax[wave * 64 + lane] = e_lo < e_hi ? m_w : -INFINITY;
     wsum[wave * 64 + lane] = s_w;
   }
   __syncthreads();
 
-  // ---- merge (wave 0): global top-kk, softmax, gates --------------------------
+  // ---- 2. merge (wave 0): global top-kk, softmax, gates --------------------------
   if (wave == 0) {
-    float sel_v[9];
-    int sel_i[9];
-    float pv = INFINITY;
-    int pi = -1;
+    const int64_t t = t0 + lane;
+    float sel_v[KK];
+    int sel_i[KK];
+    uint64_t heads = 0;  // 4 bits per list: index of its next candidate
 #pragma unroll
-    for (int r = 0; r < 9; ++r) {
-      if (r >= kk) break;
+    for (int r = 0; r < KK; ++r) {
       float best = -INFINITY;
-      int bi = 0x7FFFFFFF;
-      for (int q = 0; q < nw * kk; ++q) {
-        const float v = cand_v[q * 64 + lane];
-        const int i = cand_i[q * 64 + lane];
+      int bi = 0x7FFFFFFF, bw = -1;
+      for (int w = 0; w < NW; ++w) {
+        const int h = (int)((heads >> (4 * w)) & 15u);
+        if (h >= KK) continue;
+        const float v = cand_v[(w * KK + h) * 64 + lane];
+        const int i = cand_i[(w * KK + h) * 64 + lane];
         if (i == 0x7FFFFFFF) continue;
-        if (!(v < pv || (v == pv && i > pi))) continue;  // already taken: not after the previous pick
-        if (bi == 0x7FFFFFFF || better(v, i, best, bi)) {
+        if (bw < 0 || better(v, i, best, bi)) {
           best = v;
           bi = i;
+          bw = w;
         }
       }
+      if (bw >= 0) heads += uint64_t(1) << (4 * bw);
       sel_v[r] = best;
       sel_i[r] = bi;
-      pv = best;
-      pi = bi;
     }
     float m = -INFINITY;
-    for (int w = 0; w < nw; ++w) m = fmaxf(m, wmax[w * 64 + lane]);
+    for (int w = 0; w < NW; ++w) m = fmaxf(m, wmax[w * 64 + lane]);
     float S = 0.0f;
-    for (int w = 0; w < nw; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = wmax[w * 64 + lane];
       if (mw != -INFINITY) S += wsum[w * 64 + lane] * expf(mw - m);
     }
@@ -282,40 +460,40 @@ __global__ __launch_bounds__(1024) void route_kernel(RouteArgs a) {
     if (a.renormalize) {
       float den = 0.0f, num[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < KS; ++s) {
         if (s >= k) break;
         num[s] = expf(sel_v[s] - sel_v[0]);
         den += num[s];
       }
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < KS; ++s) {
         if (s >= k) break;
         g[s] = num[s] / den;
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < KS; ++s) {
         if (s >= k) break;
         g[s] = expf(sel_v[s] - m) / S;
       }
     }
     float thr_out = 0.0f, thr_in = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 9; ++r) {
+    for (int r = 0; r < KK; ++r) {
       if (r == k - 1) thr_out = sel_v[r];
-      if (r == k && r < kk) thr_in = sel_v[r];
+      if (r == k) thr_in = sel_v[r];
     }
-    res[0 * 64 + lane] = m;
-    res[1 * 64 + lane] = 1.0f / S;
-    res[2 * 64 + lane] = thr_out;
-    res[3 * 64 + lane] = thr_in;
-    res[4 * 64 + lane] = S;
+    float* rt = res + lane * RS;
+    rt[0] = m;
+    rt[1] = S;
+    rt[2] = thr_out;
+    rt[3] = thr_in;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < KS; ++s) {
       if (s >= k) break;
-      reinterpret_cast<int*>(res)[(5 + s) * 64 + lane] = sel_i[s];
-      res[(13 + s) * 64 + lane] = g[s];
-      if (tok_ok) {
+      reinterpret_cast<int*>(rt)[4 + s] = sel_i[s];
+      rt[12 + s] = g[s];
+      if (t < T) {
         a.topk_idx[t * k + s] = sel_i[s];
         a.topk_gate[t * k + s] = g[s];
       }
@@ -323,52 +501,78 @@ __global__ __launch_bounds__(1024) void route_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  // ---- per-expert partial sums over the block's tokens ------------------------
-  const float m = res[0 * 64 + lane];
-  const float S = res[4 * 64 + lane];
-  const float thr_out = res[2 * 64 + lane];
-  const float thr_in = res[3 * 64 + lane];
-  const bool have_in = kk > k;
-  int sel[8];
-  float gs[8];
+  // ---- 3. lane = expert: sums over a token slice, in token order ----------------
+  const int G = (E + 63) / 64;
+  const int TS = NW / G;
+  const int TL = (64 + TS - 1) / TS;
+  const int gq = wave % G, ts = wave / G;
+  const int e = gq * 64 + lane;
+  if (ts < TS && e < E) {
+    const bool have_in = KK > k;
+    const int tl_lo = min(nt, ts * TL), tl_hi = min(nt, tl_lo + TL);
+    float p_sum = 0.0f, imp_sum = 0.0f, ld_sum = 0.0f;
+    int cnt = 0;
+    constexpr int TB = NOISY ? 8 : 16;  // tokens whose loads are in flight together
+    for (int tb = tl_lo; tb < tl_hi; tb += TB) {
+      float hb[TB], cb[TB], sb[TB];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    if (s >= k) break;
-    sel[s] = reinterpret_cast<const int*>(res)[(5 + s) * 64 + lane];
-    gs[s] = res[(13 + s) * 64 + lane];
-  }
-#pragma unroll
-  for (int c = 0; c < EPW; ++c) {
-    const int e = e0 + c;
-    const bool valid = e < E && tok_ok;
-    float p = 0.0f, imp = 0.0f, cnt = 0.0f, ld = 0.0f;
-    if (valid) {
-      p = expf(h[c] - m) / S;
-      bool in_k = false;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (s >= k) break;
-        if (sel[s] == e) {
-          in_k = true;
-          imp = gs[s];
+      for (int u = 0; u < TB; ++u) {
+        const int64_t t = t0 + min(tb + u, tl_hi - 1);
+        hb[u] = a.H[t * lpad + e];
+        if constexpr (NOISY) {
+          cb[u] = a.CL[t * lpad + e];
+          sb[u] = a.SG[t * lpad + e];
         }
       }
-      cnt = in_k ? 1.0f : 0.0f;
-      if constexpr (NOISY) {
-        ld = (in_k && !have_in) ? 1.0f : std_normal_cdf((cl[c] - (in_k ? thr_in : thr_out)) / sg[c]);
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const int tl = tb + u;
+        if (tl >= tl_hi) break;
+        const float* rt = res + tl * RS;
+        const float h = hb[u];
+        if (a.logits_out) a.logits_out[(t0 + tl) * E + e] = h;
+        p_sum += expf(h - rt[0]) / rt[1];
+        bool in_k = false;
+        float gk = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          if (s >= k) break;
+          if (reinterpret_cast<const int*>(rt)[4 + s] == e) {
+            in_k = true;
+            gk = rt[12 + s];
+          }
+        }
+        imp_sum += gk;
+        cnt += in_k ? 1 : 0;
+        if constexpr (NOISY) {
+          const float thr = in_k ? rt[3] : rt[2];
+          ld_sum += (in_k && !have_in) ? 1.0f : std_normal_cdf((cb[u] - thr) / sb[u]);
+        }
       }
     }
-    p = wave_sum(p);
-    imp = wave_sum(imp);
-    cnt = wave_sum(cnt);
-    if constexpr (NOISY) ld = wave_sum(ld);
-    if (lane == c && e < E) {
-      const int64_t o = (int64_t)e * a.nblk + blockIdx.x;
-      a.part_prob[o] = p;
-      a.part_imp[o] = imp;
-      a.part_load[o] = ld;
-      a.part_cnt[o] = (int32_t)cnt;
+    const int o = ts * (G * 64) + e;
+    part[0 * NW * 64 + o] = p_sum;
+    part[1 * NW * 64 + o] = imp_sum;
+    part[2 * NW * 64 + o] = ld_sum;
+    reinterpret_cast<int*>(part)[3 * NW * 64 + o] = cnt;
+  }
+  __syncthreads();
+  const int ef = threadIdx.x;
+  if (ef < E) {
+    float p_sum = 0.0f, imp_sum = 0.0f, ld_sum = 0.0f;
+    int cnt = 0;
+    for (int s = 0; s < TS; ++s) {
+      const int o = s * (G * 64) + ef;
+      p_sum += part[0 * NW * 64 + o];
+      imp_sum += part[1 * NW * 64 + o];
+      ld_sum += part[2 * NW * 64 + o];
+      cnt += reinterpret_cast<const int*>(part)[3 * NW * 64 + o];
     }
+    const int64_t o = (int64_t)ef * a.nblk + blockIdx.x;
+    a.part_prob[o] = p_sum;
+    a.part_imp[o] = imp_sum;
+    a.part_load[o] = ld_sum;
+    a.part_cnt[o] = cnt;
   }
 }
 
@@ -461,19 +665,65 @@ __global__ void softplus_kernel(const float* __restrict__ z, float* __restrict__
   if (i < n) out[i] = canon_softplus(z[i]);
 }
 
-int route_epw(int E) { return E <= 256 ? 16 : (E <= 512 ? 32 : 64); }
-
-template <typename Tin, bool NOISY, int EPW>
-hipError_t launch_route_t(const RouteArgs& ra, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((route_kernel<Tin, NOISY, EPW>), dim3(ra.nblk), dim3(64 * ra.nw), lds, s, ra);
+template <bool NOISY, int KK>
+hipError_t launch_select_t(const RouteArgs& ra, hipStream_t s) {
+  const size_t lds = sizeof(float) * ((size_t)2 * 16 * KK * 64 + 2 * 16 * 64 + 64 * 24 + 4 * 16 * 64);
+  hipLaunchKernelGGL((route_select_kernel<NOISY, KK>), dim3(ra.nblk), dim3(1024), lds, s, ra);
   return hipGetLastError();
 }
 
-template <typename Tin, bool NOISY>
-hipError_t launch_route_epw(int epw, const RouteArgs& ra, size_t lds, hipStream_t s) {
-  if (epw == 16) return launch_route_t<Tin, NOISY, 16>(ra, lds, s);
-  if (epw == 32) return launch_route_t<Tin, NOISY, 32>(ra, lds, s);
-  return launch_route_t<Tin, NOISY, 64>(ra, lds, s);
+template <bool NOISY>
+hipError_t launch_select(int kk, const RouteArgs& ra, hipStream_t s) {
+  switch (kk) {
+    case 1: return launch_select_t<NOISY, 1>(ra, s);
+    case 2: return launch_select_t<NOISY, 2>(ra, s);
+    case 3: return launch_select_t<NOISY, 3>(ra, s);
+    case 4: return launch_select_t<NOISY, 4>(ra, s);
+    case 5: return launch_select_t<NOISY, 5>(ra, s);
+    case 6: return launch_select_t<NOISY, 6>(ra, s);
+    case 7: return launch_select_t<NOISY, 7>(ra, s);
+    case 8: return launch_select_t<NOISY, 8>(ra, s);
+    default: return launch_select_t<NOISY, 9>(ra, s);
+  }
+}
+
+// Column block of the logits GEMM: 64 columns for small gate-only layers, else 128.
+int route_bn(int E, bool noisy) { return (!noisy && E <= 64) ? 64 : 128; }
+int route_ncol(int E, bool noisy) {
+  const int bn = route_bn(E, noisy);
+  if (noisy) return ((E + bn / 2 - 1) / (bn / 2)) * bn;
+  return ((E + bn - 1) / bn) * bn;
+}
+int route_lpad(int E) { return (E + 3) & ~3; }
+
+struct LogitBufs {
+  float *H, *CL, *SG;
+};
+LogitBufs logit_bufs(const RouteLaunch& a, bool noisy) {
+  const size_t n = (size_t)a.T * route_lpad(a.E);
+  return LogitBufs{a.lg, noisy ? a.lg + n : nullptr, noisy ? a.lg + 2 * n : nullptr};
+}
+
+template <typename Tin>
+hipError_t launch_logits(const RouteLaunch& a, bool noisy, hipStream_t s) {
+  const LogitBufs lb = logit_bufs(a, noisy);
+  const int bn = route_bn(a.E, noisy), ncol = route_ncol(a.E, noisy);
+  const int64_t nwc = (int64_t)a.d * ncol;
+  hipLaunchKernelGGL(route_prep_kernel<Tin>, dim3((unsigned)((nwc + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const Tin*>(a.w_gate), static_cast<const Tin*>(noisy ? a.w_noise : nullptr), a.wc,
+                     a.d, a.E, ncol, bn);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const dim3 grid((unsigned)((a.T + kLgTok - 1) / kLgTok), (unsigned)(ncol / bn));
+  const int lpad = route_lpad(a.E);
+  if (bn == 64) {
+    hipLaunchKernelGGL((route_logits_kernel<Tin, 64>), grid, dim3(128), 0, s, static_cast<const Tin*>(a.x), a.wc,
+                       a.T, a.d, a.E, ncol, lpad, noisy ? 1 : 0, a.gate_bias, a.noise, lb.H, lb.CL, lb.SG);
+  } else {
+    hipLaunchKernelGGL((route_logits_kernel<Tin, 128>), grid, dim3(256), 0, s, static_cast<const Tin*>(a.x), a.wc,
+                       a.T, a.d, a.E, ncol, lpad, noisy ? 1 : 0, a.gate_bias, a.noise, lb.H, lb.CL, lb.SG);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -481,52 +731,30 @@ hipError_t launch_route_epw(int epw, const RouteArgs& ra, size_t lds, hipStream_
 
 int route_tokens_per_block(int E, bool noisy) { return 64; }
 
-size_t route_weight_floats(int d, int E) {
-  const int epw = moe::route_epw(E);
-  const int epad = ((E + epw - 1) / epw) * epw;
-  return (size_t)d * epad;
-}
+size_t route_weight_floats(int d, int E, bool noisy) { return (size_t)d * moe::route_ncol(E, noisy); }
+
+size_t route_logit_floats(int64_t T, int E, bool noisy) { return (size_t)T * moe::route_lpad(E) * (noisy ? 3 : 1); }
 
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
   using namespace moe;
   const bool noisy = a.w_noise != nullptr;
-  const int epw = route_epw(a.E);
-  const int nw = (a.E + epw - 1) / epw;
-  const int epad = nw * epw;
   const int nblk = (int)((a.T + 63) / 64);
   hipError_t err = hipSuccess;
   if (a.T > 0) {
-    const int64_t nw32 = (int64_t)a.d * epad;
-    const dim3 pg((unsigned)((nw32 + 255) / 256));
-    if (a.dtype == 1) {
-      hipLaunchKernelGGL(route_prep_kernel<uint16_t>, pg, dim3(256), 0, s, static_cast<const uint16_t*>(a.w_gate),
-                         a.w32, a.d, a.E, epad);
-      if (noisy)
-        hipLaunchKernelGGL(route_prep_kernel<uint16_t>, pg, dim3(256), 0, s,
-                           static_cast<const uint16_t*>(a.w_noise), a.wn32, a.d, a.E, epad);
-    } else {
-      hipLaunchKernelGGL(route_prep_kernel<float>, pg, dim3(256), 0, s, static_cast<const float*>(a.w_gate), a.w32,
-                         a.d, a.E, epad);
-      if (noisy)
-        hipLaunchKernelGGL(route_prep_kernel<float>, pg, dim3(256), 0, s, static_cast<const float*>(a.w_noise),
-                           a.wn32, a.d, a.E, epad);
-    }
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    err = a.dtype == 1 ? launch_logits<uint16_t>(a, noisy, s) : launch_logits<float>(a, noisy, s);
+    if (err != hipSuccess) return err;
     RouteArgs ra;
     ra.T = a.T;
-    ra.d = a.d;
     ra.E = a.E;
-    ra.epad = epad;
+    ra.lpad = route_lpad(a.E);
     ra.k = a.k;
-    ra.kk = noisy ? (a.k + 1 < a.E ? a.k + 1 : a.E) : a.k;
     ra.renormalize = a.renormalize;
     ra.nblk = nblk;
-    ra.nw = nw;
-    ra.x = a.x;
-    ra.w32 = a.w32;
-    ra.wn32 = noisy ? a.wn32 : nullptr;
-    ra.gate_bias = a.gate_bias;
-    ra.noise = a.noise;
+    ra.epw = ((a.E + 16 * 4 - 1) / (16 * 4)) * 4;  // experts per wave in the scan: 16 waves, multiple of 4
+    const LogitBufs lb = logit_bufs(a, noisy);
+    ra.H = lb.H;
+    ra.CL = lb.CL;
+    ra.SG = lb.SG;
     ra.topk_idx = a.topk_idx;
     ra.topk_gate = a.topk_gate;
     ra.logits_out = a.logits_out;
@@ -534,12 +762,8 @@ hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
     ra.part_imp = a.part_imp;
     ra.part_load = a.part_load;
     ra.part_cnt = a.part_cnt;
-    const size_t lds = sizeof(float) * ((size_t)2 * nw * ra.kk * 64 + 2 * nw * 64 + 21 * 64);
-    if (a.dtype == 1) {
-      err = noisy ? launch_route_epw<uint16_t, true>(epw, ra, lds, s) : launch_route_epw<uint16_t, false>(epw, ra, lds, s);
-    } else {
-      err = noisy ? launch_route_epw<float, true>(epw, ra, lds, s) : launch_route_epw<float, false>(epw, ra, lds, s);
-    }
+    const int kk = noisy ? (a.k + 1 < a.E ? a.k + 1 : a.E) : a.k;
+    err = noisy ? launch_select<true>(kk, ra, s) : launch_select<false>(kk, ra, s);
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(route_reduce_kernel, dim3(a.E), dim3(256), 0, s, a.part_prob, a.part_imp, a.part_load,
