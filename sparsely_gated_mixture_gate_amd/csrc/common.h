@@ -109,6 +109,7 @@ hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s);
 struct FfnLaunch {
   int d, f, E, dtype, act;
   int64_t max_rows;
+  int64_t capacity;  // rows per expert at most (< 0: unlimited)
   const void* x_perm;
   const int32_t* offsets;
   const void* w1;

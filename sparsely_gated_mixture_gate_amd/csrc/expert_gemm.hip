@@ -127,28 +127,34 @@ __device__ __forceinline__ int swz_a_rc(int row) {
 }
 
 // C[rows of segment e] = act?(A . W[e]); A [R][K], W [E][K][N], C [R][N], all bf16.
-// BM x 256 x BK tiles, 512 threads = 2 x 4 waves of (BM/2) x 64, NSTAGE-deep
-// LDS ring fed by direct-to-LDS buffer loads (NSTAGE - 1 k-tiles in flight).
-template <int BM, int BK, int NSTAGE, int ACT, bool APPLY_ACT>
+// BM x BN x BK tiles (BN = 256 or 128), 512 threads = (8 / (BN/64)) x (BN/64)
+// waves of 64 columns each, NSTAGE-deep LDS ring fed by direct-to-LDS buffer
+// loads (NSTAGE - 1 k-tiles in flight).
+template <int BM, int BN, int BK, int NSTAGE, int ACT, bool APPLY_ACT, bool SKIP>
 __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                                 const uint16_t* __restrict__ W,
                                                                 uint16_t* __restrict__ C,
                                                                 const int32_t* __restrict__ offsets,
                                                                 const int32_t* __restrict__ tile_start, int E,
                                                                 int K, int N, int n_tiles_n) {
-  constexpr int BN = 256;
-  constexpr int WM = BM / 2;             // wave tile rows
+  constexpr int WN_W = BN / 64;          // waves along N
+  constexpr int WM_W = 8 / WN_W;         // waves along M
+  constexpr int BCR = BN / 8;            // 16-byte chunks per B row
+  constexpr int WM = BM / WM_W;          // wave tile rows
   constexpr int MI = WM / 16;            // 16-row MFMA tiles per wave
   constexpr int NI = 4;                  // 16-column MFMA tiles per wave (64 columns)
   constexpr int RC = BK / 8;             // 16-byte chunks per A row
   constexpr int A_CH = BM * RC;          // chunks per A tile
-  constexpr int B_CH = BK * 32;          // chunks per B tile (256 columns = 32 chunks per row)
-  constexpr int A_LD = A_CH / 512;       // loads per thread per tile
+  constexpr int B_CH = BK * BCR;         // chunks per B tile
+  constexpr int A_LD = (A_CH + 511) / 512;  // A loads per thread per tile (the last round may be partial)
+  constexpr int A_TAIL_W = (A_CH % 512) / 64;  // waves that issue the partial last round (0: none)
   constexpr int B_LD = B_CH / 512;
-  constexpr int LD = A_LD + B_LD;
+  constexpr int LD_HI = A_LD + B_LD;                       // loads per tile of waves < A_TAIL_W
+  constexpr int LD_LO = A_LD - (A_TAIL_W ? 1 : 0) + B_LD;  // loads per tile of the other waves
   constexpr int STAGE_CH = A_CH + B_CH;
-  static_assert(A_CH % 512 == 0 && B_CH % 512 == 0, "tile / thread mismatch");
+  static_assert(A_CH % 64 == 0 && B_CH % 512 == 0, "tile / thread mismatch");
   static_assert(NSTAGE >= 2 && NSTAGE <= 5, "stages");
+  static_assert((BN == 128 || BN == 256) && WM % 16 == 0, "tile shape");
   __shared__ uint4 smem[NSTAGE * STAGE_CH];
 
   int e, row0, row_end, nt;
@@ -180,11 +186,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
     const int lrow = min(row, rows - 1);
     voffA[i] = (lrow * K + kc * 8) * 2;
     voffA_last[i] = (lrow * K + min(kc * 8, K - k_last - 8)) * 2;  // + soffset k_last*2
+    if (SKIP && row >= rows) voffA[i] = voffA_last[i] = kOut;  // rows past the segment load zero
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
     const int c = tid + 512 * i;
-    const int kr = c >> 5, phys = c & 31;
+    const int kr = c / BCR, phys = c % BCR;
     const int nc = phys ^ (2 * swz_b(kr));
     const int gn = n0 + nc * 8;
     voffB[i] = gn < N ? (kr * N + gn) * 2 : kOut;
@@ -199,6 +206,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
     const int soffB = kt * BK * N * 2;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
+      if (A_TAIL_W && i == A_LD - 1 && wave >= A_TAIL_W) break;
       const uint32_t dst = lds0 + (uint32_t)((st * STAGE_CH + i * 512 + wave * 64) * 16);
       load_to_lds(__builtin_amdgcn_readfirstlane(dst), last ? voffA_last[i] : voffA[i], rsA, soffA);
     }
@@ -209,7 +217,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
     }
   };
 
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WN_W, wn = wave % WN_W;
+  // SKIP: 16-row MFMA tiles wholly past the segment are neither read nor multiplied
+  const int mact = SKIP ? __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - wm * WM + 15) / 16))) : MI;
   const int g = lane >> 4;   // k-group of 8 inside a 32-wide k step
   const int s = lane & 15;
   floatx4 acc[MI][NI];
@@ -229,7 +239,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
       for (int mi = 0; mi < MI; ++mi) {
         const int row = wm * WM + mi * 16 + s;
         const int ch = ks * 4 + g;
-        af[mi] = __builtin_bit_cast(bf16x8, sA[row * RC + (ch ^ swz_a_rc<RC>(row))]);
+        if (mi < mact) af[mi] = __builtin_bit_cast(bf16x8, sA[row * RC + (ch ^ swz_a_rc<RC>(row))]);
       }
       // Transposing LDS read: source lane s of each 16-lane group points at row
       // k0 + s/4, columns n + 4*(s%4) .. +3; lane L of the group then receives
@@ -239,8 +249,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
         const int krow = ks * 32 + 8 * g + (s >> 2);
         const int ncol = wn * 64 + ni * 16 + 4 * (s & 3);
         const int c = ncol >> 3;
-        const int b0 = krow * 512 + ((c ^ (2 * swz_b(krow))) << 4) + ((ncol & 7) << 1);
-        const int b1 = (krow + 4) * 512 + ((c ^ (2 * swz_b(krow + 4))) << 4) + ((ncol & 7) << 1);
+        const int b0 = krow * (BN * 2) + ((c ^ (2 * swz_b(krow))) << 4) + ((ncol & 7) << 1);
+        const int b1 = (krow + 4) * (BN * 2) + ((c ^ (2 * swz_b(krow + 4))) << 4) + ((ncol & 7) << 1);
         const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b0));
         const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b1));
         const short __attribute__((ext_vector_type(8))) both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -249,10 +259,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
       // swapped operands: D[n][m] = sum_k W[k][n] A[m][k], so each lane ends with
       // 4 consecutive output columns of one row
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi) {
+        if (mi >= mact) break;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+      }
     }
   };
 
@@ -260,7 +272,10 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
   for (int t = 0; t < NSTAGE - 1; ++t)
     if (t < nk) issue(t);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_tiles<LD, NSTAGE - 2>(min(NSTAGE - 2, nk - 1 - kt));
+    if (A_TAIL_W == 0 || wave < A_TAIL_W)
+      wait_tiles<LD_HI, NSTAGE - 2>(min(NSTAGE - 2, nk - 1 - kt));
+    else
+      wait_tiles<LD_LO, NSTAGE - 2>(min(NSTAGE - 2, nk - 1 - kt));
     block_barrier();  // tile kt is in LDS for every wave; buffer of tile kt-1 is free
     if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1);
     compute(kt % NSTAGE);
@@ -343,7 +358,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
   }
 }
 
-template <int BM, int BK, int NSTAGE, int ACT>
+// Grid rounded up to a multiple of the XCD count (surplus workgroups exit at once).
+dim3 grid_for(int64_t tiles) { return dim3((unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds)); }
+
+template <int BM, int BK, int NSTAGE, int ACT, bool SKIP>
 hipError_t launch_bf16(const FfnLaunch& a, hipStream_t s) {
   constexpr int BN = 256;
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, BM, a.tile_start);
@@ -351,13 +369,12 @@ hipError_t launch_bf16(const FfnLaunch& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   const int64_t mtiles = (a.max_rows + BM - 1) / BM + a.E;
   const int nt1 = (a.f + BN - 1) / BN, nt2 = (a.d + BN - 1) / BN;
-  auto grid = [](int64_t tiles) { return dim3((unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds)); };
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BK, NSTAGE, ACT, true>), grid(mtiles * nt1), dim3(512), 0, s,
-                     static_cast<const uint16_t*>(a.x_perm), static_cast<const uint16_t*>(a.w1),
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, true, SKIP>), grid_for(mtiles * nt1),
+                     dim3(512), 0, s, static_cast<const uint16_t*>(a.x_perm), static_cast<const uint16_t*>(a.w1),
                      static_cast<uint16_t*>(a.h1), a.offsets, a.tile_start, a.E, a.d, a.f, nt1);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BK, NSTAGE, ACT, false>), grid(mtiles * nt2), dim3(512), 0, s,
-                     static_cast<const uint16_t*>(a.h1), static_cast<const uint16_t*>(a.w2),
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, false, SKIP>), grid_for(mtiles * nt2),
+                     dim3(512), 0, s, static_cast<const uint16_t*>(a.h1), static_cast<const uint16_t*>(a.w2),
                      static_cast<uint16_t*>(a.y_perm), a.offsets, a.tile_start, a.E, a.f, a.d, nt2);
   return hipGetLastError();
 }
@@ -383,11 +400,16 @@ hipError_t launch_f32(const FfnLaunch& a, hipStream_t s) {
 template <int ACT>
 hipError_t launch_ffn_act(const FfnLaunch& a, hipStream_t s) {
   if (a.dtype != 1) return launch_f32<ACT>(a, s);
-  // Expected rows per expert decides the M tile: weight-streaming experts
-  // (about one tile of rows each) take 128-row tiles, large segments 256.
+  // A capacity of at most 160 (256) rows puts every expert in one 160-row
+  // (256-row) M-tile, so each weight panel is streamed once; MFMA tiles past the
+  // segment are skipped.
+  if (a.capacity >= 0 && a.capacity <= 160) return launch_bf16<160, 64, 3, ACT, true>(a, s);
+  if (a.capacity >= 0 && a.capacity <= 256) return launch_bf16<256, 32, 4, ACT, true>(a, s);
+  // Otherwise the expected rows per expert decide the M tile: weight-streaming
+  // experts (about one tile of rows each) take 128-row tiles, large segments 256.
   const int64_t rows_per_expert = a.max_rows / a.E;
-  if (rows_per_expert >= 512) return launch_bf16<256, 32, 4, ACT>(a, s);
-  return launch_bf16<128, 64, 3, ACT>(a, s);
+  if (rows_per_expert >= 512) return launch_bf16<256, 32, 4, ACT, false>(a, s);
+  return launch_bf16<128, 64, 3, ACT, false>(a, s);
 }
 
 }  // namespace

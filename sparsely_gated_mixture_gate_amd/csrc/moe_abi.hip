@@ -260,6 +260,7 @@ moe_status run_ffn(const moe_params* p, const void* x_perm, const int32_t* offse
   a.dtype = p->dtype;
   a.act = p->act;
   a.max_rows = max_rows_of(p);
+  a.capacity = capacity_of(p);
   a.x_perm = x_perm;
   a.offsets = offsets;
   a.w1 = w1;
