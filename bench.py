@@ -148,9 +148,14 @@ def pmc_report(fetch_dir, write_dir, out_json, config, calib_mib):
     kib = calib_mib * 1024.0
     f_scale = kib / mean(fetch, is_copy)
     w_scale = kib / mean(write, is_copy)
+    def applies_act(k):
+        # grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, APPLY_ACT, SKIP> / grouped_gemm_f32_kernel<ACT, APPLY_ACT>
+        targs = [t.strip() for t in k[k.index("<") + 1:k.index(">")].split(",")]
+        return targs[5] == "true" if "bf16" in k else targs[1] == "true"
+
     parts = {}
-    for tag, pred in (("gemm1", lambda k: "grouped_gemm" in k and "true>" in k),
-                      ("gemm2", lambda k: "grouped_gemm" in k and "false>" in k),
+    for tag, pred in (("gemm1", lambda k: "grouped_gemm" in k and applies_act(k)),
+                      ("gemm2", lambda k: "grouped_gemm" in k and not applies_act(k)),
                       ("tile_map", lambda k: "tile_map_kernel" in k)):
         f_kib, w_kib = mean(fetch, pred), mean(write, pred)
         parts[tag] = {"fetch_bytes": f_kib * 1024 * f_scale, "write_bytes": w_kib * 1024 * w_scale,
