@@ -60,6 +60,7 @@ typedef enum moe_status {
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 enum { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1 }; /* GELU is the exact 0.5 z (1 + erf(z / sqrt 2)) */
 enum { MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2, MOE_OP_FORWARD = 3 };
+enum { MOE_GATE_AUTO = 0, MOE_GATE_CANONICAL = 1, MOE_GATE_FALLBACK = 2 };
 
 typedef struct moe_params {
   int64_t T;               /* tokens in the batch */
@@ -71,7 +72,14 @@ typedef struct moe_params {
   int32_t act;             /* MOE_ACT_RELU or MOE_ACT_GELU */
   int32_t renormalize;     /* 1: gates = softmax over the k kept logits (Shazeer, KeepTopK + Softmax);
                               0: gates = full-softmax probabilities of the kept experts (Switch listing) */
-  int32_t reserved;        /* must be 0 */
+  int32_t gate_mode;       /* how moe_route / moe_forward evaluate the gate logits (MOE_GATE_*):
+                              MOE_GATE_AUTO (0): bf16 layers with E <= 256 compute the logits with
+                                bf16 MFMAs and certify each token's top-k against the canonical
+                                logits (below); uncertified tokens, fp32 layers, E > 256 and calls
+                                with logits_out use the canonical fp32 chains;
+                              MOE_GATE_CANONICAL (1): canonical fp32 chains for every token;
+                              MOE_GATE_FALLBACK (2): the MFMA path with every token sent through its
+                                canonical fallback (testing). Routing is identical in all modes. */
   double capacity_factor;  /* > 0: per-expert capacity C = ceil(capacity_factor * k * T / E); <= 0: none */
   int64_t capacity;        /* >= 0: explicit per-expert capacity C (overrides capacity_factor); < 0: unused */
 } moe_params;
@@ -109,6 +117,16 @@ moe_status moe_workspace_size(const moe_params* p, int op, size_t* bytes);
  * Experts are ordered by H descending, ties to the lower index; slot s < k
  * takes the s-th. Gates (fp32): renormalize=1: softmax over the kept logits;
  * 0: full-softmax probability.
+ * Certified MFMA gate (gate_mode AUTO, bf16, E <= 256, logits_out NULL): the
+ * logits are computed with bf16 MFMAs (exact products, fp32 sums in the
+ * hardware's order) together with sum_j |x[t,j] w[j,e]|, which bounds the
+ * distance B to the canonical value (4 d 2^-24 sum|x w| plus the rounding of the
+ * bias add, softplus and fma). A token whose k gaps between consecutive values
+ * of its top-(k+1) all exceed twice its largest B has the canonical routing;
+ * every other token is recomputed with the canonical chains. topk_idx and
+ * counts_routed are therefore those of the canonical logits in every mode; the
+ * gates, aux losses and load estimates of certified tokens use the MFMA logits
+ * (rounding-level differences).
  * Inputs:  x [T,d] dtype; w_gate [d,E] dtype; gate_bias [E] fp32 or NULL;
  *          w_noise [d,E] dtype or NULL; noise [T,E] fp32 standard normals
  *          (required iff w_noise).

@@ -21,6 +21,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
 MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_FORWARD = range(4)
+MOE_GATE_AUTO, MOE_GATE_CANONICAL, MOE_GATE_FALLBACK = range(3)
 
 EXPORTED = (
     "moe_status_string", "moe_last_error", "moe_capacity", "moe_max_rows", "moe_workspace_size",
@@ -44,7 +45,7 @@ class moe_params(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("act", ctypes.c_int32),
         ("renormalize", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("gate_mode", ctypes.c_int32),
         ("capacity_factor", ctypes.c_double),
         ("capacity", ctypes.c_int64),
     ]
@@ -120,11 +121,11 @@ def status_string(status: int) -> str:
 
 
 def make_params(T, d_model, d_ff, E, k, dtype="bf16", act="gelu", renormalize=False, capacity_factor=0.0,
-                capacity=-1) -> moe_params:
+                capacity=-1, gate_mode=0) -> moe_params:
     return moe_params(int(T), int(d_model), int(d_ff), int(E), int(k),
                       MOE_BF16 if dtype in ("bf16", MOE_BF16) else MOE_F32,
                       MOE_ACT_GELU if act in ("gelu", MOE_ACT_GELU) else MOE_ACT_RELU,
-                      int(bool(renormalize)), 0, float(capacity_factor), int(capacity))
+                      int(bool(renormalize)), int(gate_mode), float(capacity_factor), int(capacity))
 
 
 def moe_capacity(p: moe_params) -> int:

@@ -78,6 +78,8 @@ struct RouteLaunch {
   // workspace pieces
   float* wc;         // [d][ncol] fp32 gate (and noise) weights in column blocks
   float* lg;         // route_logit_floats(T, E, noisy): logits H [, clean logits, softplus of noise logits]
+  uint16_t* wcat;    // route_wcat_elems(d, E, noisy): bf16 gate (+ noise) weights of the MFMA gate
+  int gate_mode;     // MOE_GATE_*
   float* part_prob;  // [E][nblk]
   float* part_imp;   // [E][nblk]
   float* part_load;  // [E][nblk]
@@ -88,6 +90,10 @@ int route_tokens_per_block(int E, bool noisy);
 size_t route_weight_floats(int d, int E, bool noisy);
 size_t route_logit_floats(int64_t T, int E, bool noisy);
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
+bool route_fused_supported(int dtype, int E);
+size_t route_wcat_elems(int d, int E, bool noisy);
+hipError_t launch_route_fused(const RouteLaunch& a, bool noisy, int force_fallback, float* CL, float* SG, int lpad,
+                              hipStream_t s);
 
 struct DispatchLaunch {
   int64_t T;

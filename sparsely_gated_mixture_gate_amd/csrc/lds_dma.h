@@ -44,6 +44,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 // issued after the one about to be read, LD = loads per thread per tile).
 template <int LD, int MAXREM>
 __device__ __forceinline__ void wait_tiles(int rem) {
+  static_assert(MAXREM * LD < 64, "vmcnt range");
+  if constexpr (MAXREM >= 7) {
+    if (rem >= 7) { wait_vmcnt<7 * LD>(); return; }
+  }
+  if constexpr (MAXREM >= 6) {
+    if (rem >= 6) { wait_vmcnt<6 * LD>(); return; }
+  }
+  if constexpr (MAXREM >= 5) {
+    if (rem >= 5) { wait_vmcnt<5 * LD>(); return; }
+  }
+  if constexpr (MAXREM >= 4) {
+    if (rem >= 4) { wait_vmcnt<4 * LD>(); return; }
+  }
   if constexpr (MAXREM >= 3) {
     if (rem >= 3) { wait_vmcnt<3 * LD>(); return; }
   }

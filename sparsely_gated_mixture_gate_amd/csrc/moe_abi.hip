@@ -49,7 +49,8 @@ moe_status check_params(const moe_params* p) {
   if (p->act != MOE_ACT_RELU && p->act != MOE_ACT_GELU) return fail(MOE_ERR_INVALID_ARG, "act = %d", p->act);
   if (p->renormalize != 0 && p->renormalize != 1)
     return fail(MOE_ERR_INVALID_ARG, "renormalize = %d (0 or 1)", p->renormalize);
-  if (p->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "reserved = %d (must be 0)", p->reserved);
+  if (p->gate_mode < MOE_GATE_AUTO || p->gate_mode > MOE_GATE_FALLBACK)
+    return fail(MOE_ERR_INVALID_ARG, "gate_mode = %d (0, 1 or 2)", p->gate_mode);
   if (p->T * (int64_t)p->k >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*k = %lld >= 2^31", (long long)(p->T * p->k));
   if (isnan(p->capacity_factor)) return fail(MOE_ERR_INVALID_ARG, "capacity_factor is NaN");
@@ -97,6 +98,7 @@ struct Carver {
 
 struct RouteWs {
   float *wc, *lg;
+  uint16_t* wcat;
   float *part_prob, *part_imp, *part_load;
   int32_t* part_cnt;
   double* red;
@@ -107,6 +109,7 @@ RouteWs carve_route(Carver& c, const moe_params* p, bool noisy) {
   const size_t n = (size_t)p->E * (size_t)(nblk > 0 ? nblk : 1);
   RouteWs w;
   w.wc = c.take<float>(route_weight_floats(p->d_model, p->E, noisy));
+  w.wcat = c.take<uint16_t>(route_wcat_elems(p->d_model, p->E, noisy));
   w.lg = c.take<float>(route_logit_floats(p->T, p->E, noisy));
   w.part_prob = c.take<float>(n);
   w.part_imp = c.take<float>(n);
@@ -218,6 +221,8 @@ moe_status run_route(const moe_params* p, const void* x, const void* w_gate, con
   a.aux_out = aux_out;
   a.logits_out = logits_out;
   a.wc = w.wc;
+  a.wcat = w.wcat;
+  a.gate_mode = p->gate_mode;
   a.lg = w.lg;
   a.part_prob = w.part_prob;
   a.part_imp = w.part_imp;

@@ -1,0 +1,860 @@
+// route_mfma.hip -- the gate on the bf16 MFMA units, with a certified top-k.
+//
+// Method (Shazeer et al. summary page, "Methode": Noisy Top-K Gating; "Switch
+// Transformer" page: softmax over all experts, top-1): H = x W_g (+ b)
+// (+ eps * Softplus(x W_noise)), G = Softmax(KeepTopK(H, k)) or the softmax
+// probability of the kept experts.
+//
+// The routing decision is defined on the canonical fp32 logits (each logit an
+// ascending-j fma chain from +0). Bit-for-bit, that chain needs the fp32 VALU;
+// this kernel instead computes the logits with bf16 MFMAs (x and the weights
+// are bf16, so every product p_j = x_j w_j is exact and only the order of the
+// fp32 sums differs) and proves, token by token, that the canonical top-k is
+// the same. Running-error bound (u = 2^-24, M = ceil(d / 32) MFMA k-steps,
+// acc_m = the MFMA accumulator after step m, S = sum_j |p_j|, Q = sum_m |acc_m|):
+//   * canonical chain s_j = fl(s_{j-1} + p_j): |s_d - sum p| <= u sum_j |s_j|, and
+//     sum_j |s_j| <= (32 sum_m |exact partial after 32m terms| + 32 S) / (1 - d u);
+//   * MFMA: assume each step adds its 32 products to the accumulator with an
+//     error of at most 64 u (|acc_{m-1}| + sum of the step's |p_j|) (32 roundings,
+//     even truncating ones, or one alignment per product), so the exact partial
+//     sums are within 64 u (Q + S) of the acc_m;
+//   together |acc_M - s_d| <= 96 u (Q + S)(1 + 64 u M) / (1 - d u), used as
+//   B = 100 u (Q + S)(1 + 256 u M). S comes from a second MFMA on the
+// sign-cleared operands in the same pass; Q is summed after every step. The
+// bias add, the softplus (within 16 ulp of the true function, 1-Lipschitz) and
+// the fma with eps add their own rounding terms. If, for the top-(k+1) MFMA
+// values v_1 >= ..., every gap v_r - v_{r+1} (r = 1..k) exceeds twice the
+// token's largest B, the canonical values keep the same order and the same
+// top-k set, so the token's routing is the canonical one. Other tokens (and
+// every token when the caller asks for it) recompute their logits with the
+// canonical chains inside the block and are selected again. Gate values of
+// certified tokens use the MFMA logits (their deviation from the canonical-logit
+// gates is a rounding-level effect, far inside the bf16 output tolerance).
+//
+// One block = 64 tokens, 512 threads (8 waves):
+//   GEMM: x tile [64][32] and weight tile [32][NCOL] per stage in an LDS ring
+//   of up to 8 stages (direct-to-LDS buffer loads), v_mfma_f32_16x16x32_bf16 with
+//   swapped operands (lane = 4 consecutive columns of one token); noisy: each
+//   wave's 64 columns are 32 experts' gate columns and the same experts' noise
+//   columns, so one lane holds both halves of an expert's logit.
+//   Epilogue: bias, softplus, H, bound; H to LDS, per-token max bound.
+//   Selection, merge, certification, fallback, per-expert partial sums as in
+//   route_select (route.hip).
+#include "common.h"
+#include "lds_dma.h"
+#include "route_common.h"
+
+#include <type_traits>
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int kTok = 64;     // tokens per block
+constexpr int kBK = 32;      // k per LDS stage (one MFMA k-step)
+
+// bf16 weight copy [d][ncol]: gate only: column c = expert c; noisy: block q of
+// 64 columns = gate columns of experts 32q .. 32q+31, then their noise columns.
+// Zero past E.
+__global__ __launch_bounds__(256) void route_wcat_kernel(const uint16_t* __restrict__ wg,
+                                                         const uint16_t* __restrict__ wn,
+                                                         uint16_t* __restrict__ wcat, int d, int E, int ncol) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)d * ncol) return;
+  const int64_t j = i / ncol;
+  const int c = (int)(i - j * ncol);
+  const uint16_t* src = wg;
+  int e = c;
+  if (wn) {
+    e = 32 * (c >> 6) + (c & 31);
+    if (c & 32) src = wn;
+  }
+  wcat[i] = e < E ? src[j * E + e] : (uint16_t)0;
+}
+
+__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }  // x tile: 4 chunks per row
+
+// Fast functions for the approximate (MFMA-logit) path: gates, probabilities
+// and load estimates of certified tokens, which are compared within tolerance.
+__device__ __forceinline__ float fast_exp(float y) { return __builtin_amdgcn_exp2f(y * 1.4426950408889634f); }
+// softplus within 2^-20 + 2^-21 SP(z) of the true function (hardware exp2 / log2)
+__device__ __forceinline__ float fast_softplus(float z) {
+  if (z > 20.0f) return z;
+  const float v = fast_exp(-fabsf(z));
+  const float r = __builtin_amdgcn_logf(1.0f + v) * 0.69314718055994531f;
+  return fmaxf(z, 0.0f) + r;
+}
+// Phi(z) = erfc(-z / sqrt 2) / 2 with erfc from Abramowitz & Stegun 7.1.26 (|error| <= 1.5e-7)
+__device__ __forceinline__ float fast_normal_cdf(float z) {
+  const float a = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
+  float p = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  p = __builtin_fmaf(p, t, 1.421413741f);
+  p = __builtin_fmaf(p, t, -0.284496736f);
+  p = __builtin_fmaf(p, t, 0.254829592f);
+  const float q = p * t * fast_exp(-(a * a));  // erfc(a)
+  return z >= 0.0f ? 1.0f - 0.5f * q : 0.5f * q;
+}
+template <int BCR>
+__device__ __forceinline__ int swz_w(int k) {  // weight tile: even XOR inside the row's BCR chunks
+  return (2 * ((k & 3) | (((k >> 3) & 1) << 2))) & (BCR - 2);
+}
+
+// wait until at most rem stages (of ld loads each) of this wave are in flight
+template <int MAXREM>
+__device__ __forceinline__ void wait_stages(int ld, int rem) {
+  switch (ld) {
+    case 1: wait_tiles<1, MAXREM>(rem); break;
+    case 2: wait_tiles<2, MAXREM>(rem); break;
+    case 3: wait_tiles<3, MAXREM>(rem); break;
+    case 4: wait_tiles<4, MAXREM>(rem); break;
+    default: wait_tiles<5, MAXREM>(rem); break;
+  }
+}
+
+struct FusedArgs {
+  int64_t T;
+  int d, E, k, renormalize, nblk, force_fallback, lpad;
+  const uint16_t* x;
+  const uint16_t* wcat;
+  const float* bias;
+  const float* noise;
+  int32_t* topk_idx;
+  float* topk_gate;
+  float* CL;  // [T][lpad] clean logits (noisy)
+  float* SG;  // [T][lpad] softplus of the noise logits (noisy)
+  float* part_prob;
+  float* part_imp;
+  float* part_load;
+  int32_t* part_cnt;
+};
+
+template <int EP, bool NOISY, int KK>
+__global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
+  constexpr int NCOL = NOISY ? 2 * EP : EP;
+  constexpr int NI = NCOL == 64 ? 2 : 4;   // 16-column MFMA tiles per wave
+  constexpr int WN_W = NCOL / (16 * NI);   // waves along columns
+  constexpr int WM_W = 8 / WN_W;           // waves along tokens
+  constexpr int MI = 4 / WM_W;             // 16-token MFMA tiles per wave
+  constexpr int BCR = NCOL / 8;            // 16-byte chunks per weight row
+  constexpr int A_CH = kTok * 4;           // x chunks per stage
+  constexpr int B_CH = kBK * BCR;          // weight chunks per stage
+  constexpr int CH = A_CH + B_CH;
+  constexpr int NR = (CH + 511) / 512;     // load rounds per stage
+  constexpr int HS = EP + 1;               // LDS row stride of the logit tile (floats)
+  constexpr int EPW = EP / 8;              // experts per wave in the scan
+  constexpr int KS = KK < 8 ? KK : 8;      // selectable slots
+  constexpr int RS = 24;                   // res floats per token: m, S, thr_out, thr_in, sel[8], gate[8], pad
+  static_assert(CH % 64 == 0 && WN_W * WM_W == 8 && MI >= 1 && (!NOISY || NI == 4), "shape");
+  // GEMM ring depth: as many 32-k stages as fit beside the other LDS use (at most 8)
+  constexpr int kStages = (144 * 1024) / (CH * 16) < 8 ? (144 * 1024) / (CH * 16) : 8;
+  static_assert(kStages >= 3, "ring");
+  constexpr int RING = kStages * CH * 16;
+  // After the GEMM the ring's LDS holds: the logit tile H and the per-token
+  // results (live to the end), then the selection state, which the fallback's
+  // own ring overwrites (the selection is redone after it).
+  constexpr int OFF_RES = kTok * HS * 4;
+  constexpr int OFF_CV = OFF_RES + kTok * RS * 4;
+  constexpr int OFF_CI = OFF_CV + 8 * KK * 64 * 4;
+  constexpr int OFF_WM = OFF_CI + 8 * KK * 64 * 4;
+  constexpr int OFF_WS = OFF_WM + 8 * 64 * 4;
+  constexpr int OFF_PART = OFF_WS + 8 * 64 * 4;
+  constexpr int POST = OFF_PART + 4 * 512 * 4;
+  constexpr int SMEM0 = RING > POST ? RING : POST;
+  // fallback ring, from OFF_CV on: per stage the weight tile [F_BK][NCOL] and
+  // the x rows of 16 flagged tokens [16][F_BK]; F_BK = 32, or 16 / 8 where the
+  // weight tile is wide, so that at least 4 stages fit the free LDS
+  constexpr int FR = 16;                         // tokens per fallback round
+  constexpr int F_FREE = SMEM0 - OFF_CV;
+  constexpr int F_BK = F_FREE / ((32 * BCR + FR * 4) * 16) >= 4 ? 32
+                     : (F_FREE / ((16 * BCR + FR * 2) * 16) >= 4 ? 16 : 8);
+  constexpr int F_CPR = F_BK / 8;                // x chunks per row per stage
+  constexpr int F_WCH = F_BK * BCR;              // weight chunks per stage
+  constexpr int F_XCH = FR * F_CPR;              // x chunks per stage
+  constexpr int F_CH = F_WCH + F_XCH;            // chunks per fallback stage
+  constexpr int F_NR = (F_CH + 511) / 512;
+  constexpr int F_STAGES = F_FREE / (F_CH * 16) < 8 ? F_FREE / (F_CH * 16) : 8;
+  constexpr int SMEM = SMEM0;
+  static_assert(F_WCH % 64 == 0 && F_STAGES >= 3 && SMEM + 1024 <= 160 * 1024, "LDS");
+  __shared__ uint4 smem_u4[SMEM / 16];
+  __shared__ float bmax_s[kTok];
+  __shared__ int flist_s[kTok];
+  __shared__ int nflag_s;
+  char* smem = reinterpret_cast<char*>(smem_u4);
+  float* Hs = reinterpret_cast<float*>(smem);
+  float* cand_v = reinterpret_cast<float*>(smem + OFF_CV);
+  int* cand_i = reinterpret_cast<int*>(smem + OFF_CI);
+  float* wmax = reinterpret_cast<float*>(smem + OFF_WM);
+  float* wsum = reinterpret_cast<float*>(smem + OFF_WS);
+  float* res = reinterpret_cast<float*>(smem + OFF_RES);
+  float* part = reinterpret_cast<float*>(smem + OFF_PART);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int d = a.d, E = a.E, k = a.k;
+  const int64_t T = a.T;
+  const int64_t t0 = (int64_t)blockIdx.x * kTok;
+  const int rows = (int)min<int64_t>(kTok, T - t0);
+  if (tid < kTok) bmax_s[tid] = 0.0f;
+
+  // ---- GEMM: V = x W and S = |x| |W| over the block's 64 tokens ----------------
+  const int32x4 rsX = buffer_rsrc(a.x + t0 * d, (uint32_t)rows * d * 2);
+  const int32x4 rsW = buffer_rsrc(a.wcat, (uint32_t)d * NCOL * 2);
+  int voff[NR];
+  bool isA[NR], act[NR];
+  int ld = 0;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int c = tid + 512 * i;
+    act[i] = (i * 512 + wave * 64) < CH;  // wave-uniform
+    isA[i] = (i * 512 + wave * 64) < A_CH;
+    ld += act[i] ? 1 : 0;
+    if (c < A_CH) {
+      const int row = c >> 2, p = c & 3;
+      voff[i] = min(row, rows - 1) * d * 2 + ((p ^ swz4(row)) << 4);  // rows past T: clamped, never stored
+    } else {
+      const int b = c - A_CH;
+      const int kr = b / BCR, p = b % BCR;
+      voff[i] = kr * NCOL * 2 + ((p ^ swz_w<BCR>(kr)) << 4);  // rows past d load zero
+    }
+  }
+  const uint32_t lds0 = lds_address(&smem_u4[0]);
+  // The stage offset goes into the per-lane offset so the whole offset is
+  // range-checked: x chunks past d in the last stage meet zero weight rows.
+  auto issue = [&](int kt) {
+    const int st = kt % kStages;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      if (!act[i]) continue;
+      const uint32_t dst = lds0 + (uint32_t)((st * CH + i * 512 + wave * 64) * 16);
+      if (isA[i])
+        load_to_lds(__builtin_amdgcn_readfirstlane(dst), voff[i] + kt * kBK * 2, rsX, 0);
+      else
+        load_to_lds(__builtin_amdgcn_readfirstlane(dst), voff[i] + kt * kBK * NCOL * 2, rsW, 0);
+    }
+  };
+
+  const int wm = wave / WN_W, wn = wave % WN_W;
+  const int g = lane >> 4, s = lane & 15;
+  // acc: the logits; qs: Q + S, i.e. |acc| after every k-step (the step before
+  // this one; the last is added after the loop) plus the sign-cleared MFMA
+  floatx4 acc[MI][NI], qs[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = qs[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto add_q = [&]() {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qs[i][j][r] += fabsf(acc[i][j][r]);
+  };
+
+  auto compute = [&](int st) {
+    add_q();
+    const uint4* sA = &smem_u4[st * CH];
+    lds_char* sB = (lds_char*)(&smem_u4[st * CH + A_CH]);
+    uint4 af[MI], bfr[NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = wm * (16 * MI) + mi * 16 + s;
+      af[mi] = sA[row * 4 + (g ^ swz4(row))];
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      // transposing read: lane L of a 16-lane group receives W[k0 .. k0+3][n + L]
+      const int krow = 8 * g + (s >> 2);
+      const int ncol = wn * (16 * NI) + ni * 16 + 4 * (s & 3);
+      const int c = ncol >> 3;
+      const int b0 = krow * (NCOL * 2) + ((c ^ swz_w<BCR>(krow)) << 4) + ((ncol & 7) << 1);
+      const int b1 = (krow + 4) * (NCOL * 2) + ((c ^ swz_w<BCR>(krow + 4)) << 4) + ((ncol & 7) << 1);
+      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b0));
+      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b1));
+      const short __attribute__((ext_vector_type(8))) both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      bfr[ni] = __builtin_bit_cast(uint4, both);
+    }
+    const uint4 m7 = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[ni]),
+                                                              __builtin_bit_cast(bf16x8, af[mi]), acc[mi][ni], 0, 0, 0);
+        qs[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[ni] & m7),
+                                                             __builtin_bit_cast(bf16x8, af[mi] & m7), qs[mi][ni], 0, 0, 0);
+      }
+  };
+
+  const int nk = (d + kBK - 1) / kBK;
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < nk) issue(t);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_stages<kStages - 2>(ld, min(kStages - 2, nk - 1 - kt));
+    block_barrier();
+    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+    compute(kt % kStages);
+  }
+  add_q();
+  __syncthreads();  // the ring is dead from here on; its LDS holds the logit tile and the selection state
+
+  // ---- epilogue: clean logit (+ bias), softplus, H and the bound ------------------
+  // Bound of |acc_mfma - acc_canon|: KB * (Q + S) (see the file header).
+  const float KB = 100.0f * 0x1.0p-24f * (1.0f + 256.0f * 0x1.0p-24f * (float)nk) * 1.004f;
+  // noise of this lane's (token, expert) entries, all loads in flight together
+  constexpr int NE = NOISY ? NI / 2 : NI;  // 16-expert groups per lane
+  float epsv[MI][NE][4];
+  if constexpr (NOISY) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int64_t t = min<int64_t>(t0 + wm * (16 * MI) + mi * 16 + s, T - 1);
+#pragma unroll
+      for (int ni = 0; ni < NE; ++ni) {
+        const int e = 32 * wn + 16 * ni + 4 * g;
+        if ((E & 3) == 0 && e < E) {
+          const float4 v = *reinterpret_cast<const float4*>(a.noise + t * E + e);
+          epsv[mi][ni][0] = v.x; epsv[mi][ni][1] = v.y; epsv[mi][ni][2] = v.z; epsv[mi][ni][3] = v.w;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) epsv[mi][ni][j] = e + j < E ? a.noise[t * E + e + j] : 0.0f;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int m = wm * (16 * MI) + mi * 16 + s;  // token row of this lane
+    const int64_t t = t0 + m;
+    float bmax = 0.0f;
+#pragma unroll
+    for (int ni = 0; ni < NE; ++ni) {
+      const int e0 = NOISY ? 32 * wn + 16 * ni + 4 * g : wn * (16 * NI) + ni * 16 + 4 * g;
+      float clv[4], spv[4], hv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + j;
+        float cl = acc[mi][ni][j];
+        if (a.bias && e < E) cl = cl + a.bias[e];
+        const float bcl = KB * qs[mi][ni][j] * (1.0f + 0x1.0p-22f) + 0x1.0p-22f * fabsf(cl);
+        float h = cl, bh = bcl, sp = 0.0f;
+        if constexpr (NOISY) {
+          const float zn = acc[mi][ni + 2][j];
+          sp = fast_softplus(zn);
+          const float eps = epsv[mi][ni][j];
+          h = __builtin_fmaf(eps, sp, cl);
+          // |fast_softplus(a) - canon_softplus(b)| <= |a - b| + 2^-19 SP + 2^-20 (both within their error of SP)
+          const float bn = KB * qs[mi][ni + 2][j];
+          const float bsp = bn * (1.0f + 0x1.0p-18f) + 0x1.0p-18f * sp + 0x1.0p-20f;
+          bh = (fabsf(eps) * bsp + bcl) * (1.0f + 0x1.0p-22f) + 0x1.0p-22f * fabsf(h);
+        }
+        clv[j] = cl;
+        spv[j] = sp;
+        hv[j] = e < E ? h : -INFINITY;
+        if (e < E) bmax = fmaxf(bmax, bh);
+        if (e < EP) Hs[m * HS + e] = hv[j];
+      }
+      if constexpr (NOISY) {
+        if (t < T && e0 < E) {
+          if (e0 + 3 < E) {
+            *reinterpret_cast<float4*>(a.CL + t * a.lpad + e0) = float4{clv[0], clv[1], clv[2], clv[3]};
+            *reinterpret_cast<float4*>(a.SG + t * a.lpad + e0) = float4{spv[0], spv[1], spv[2], spv[3]};
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (e0 + j < E) {
+                a.CL[t * a.lpad + e0 + j] = clv[j];
+                a.SG[t * a.lpad + e0 + j] = spv[j];
+              }
+          }
+        }
+      }
+    }
+    // lanes s, s+16, s+32, s+48 share the token row: max over them, then over waves
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    if (g == 0) atomicMax(reinterpret_cast<int*>(&bmax_s[m]), __float_as_int(bmax));  // non-negative floats order as ints
+  }
+  __syncthreads();
+
+  // ---- selection over the logit tile in LDS ---------------------------------------
+  // phase 1, lane = token: this wave's experts [wave*EPW, +EPW): top-KK, max, sum of exp
+  auto scan = [&]() {
+    const int e_lo = min(E, wave * EPW), e_hi = min(E, e_lo + EPW);
+    const float* hrow = Hs + lane * HS;
+    float bv[KK];
+    int bi[KK];
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
+      bv[r] = -INFINITY;
+      bi[r] = 0x7FFFFFFF;
+    }
+    float hv[EPW];  // all of this wave's logits of the token, read before the comparisons
+#pragma unroll
+    for (int c = 0; c < EPW; ++c) hv[c] = e_lo + c < e_hi ? hrow[e_lo + c] : -INFINITY;
+#pragma unroll
+    for (int c = 0; c < EPW; ++c) {
+      if (e_lo + c >= e_hi) break;
+      float v = hv[c];
+      int i = e_lo + c;
+      if (!better(v, i, bv[KK - 1], bi[KK - 1])) continue;
+#pragma unroll
+      for (int r = 0; r < KK; ++r) {
+        if (better(v, i, bv[r], bi[r])) {
+          const float tv = bv[r];
+          const int ti = bi[r];
+          bv[r] = v;
+          bi[r] = i;
+          v = tv;
+          i = ti;
+        }
+      }
+    }
+    const float m_w = bv[0];
+    float s_w = 0.0f;
+#pragma unroll
+    for (int c = 0; c < EPW; ++c)
+      if (e_lo + c < e_hi) s_w += fast_exp(hv[c] - m_w);
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
+      cand_v[(wave * KK + r) * 64 + lane] = bv[r];
+      cand_i[(wave * KK + r) * 64 + lane] = bi[r];
+    }
+    wmax[wave * 64 + lane] = e_lo < e_hi ? m_w : -INFINITY;
+    wsum[wave * 64 + lane] = s_w;
+  };
+
+  // phase 2 (wave 0), lane = token: merge the 8 sorted lists, softmax, gates;
+  // certify = check the gaps (first pass) or accept (canonical logits)
+  // token tl's results from its top-KK values / indices (value desc, index asc),
+  // softmax max m and sum S: gates, load-estimator thresholds, outputs
+  auto finish = [&](int tl, const float (&sel_v)[KK], const int (&sel_i)[KK], float m, float S) {
+    const int64_t t = t0 + tl;
+    float gt[8];
+    if (a.renormalize) {
+      float den = 0.0f, num[8];
+#pragma unroll
+      for (int q = 0; q < KS; ++q) {
+        if (q >= k) break;
+        num[q] = fast_exp(sel_v[q] - sel_v[0]);
+        den += num[q];
+      }
+#pragma unroll
+      for (int q = 0; q < KS; ++q) {
+        if (q >= k) break;
+        gt[q] = num[q] / den;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < KS; ++q) {
+        if (q >= k) break;
+        gt[q] = fast_exp(sel_v[q] - m) / S;
+      }
+    }
+    float thr_out = 0.0f, thr_in = 0.0f;
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
+      if (r == k - 1) thr_out = sel_v[r];
+      if (r == k) thr_in = sel_v[r];
+    }
+    float* rt = res + tl * RS;
+    rt[0] = m;
+    rt[1] = 1.0f / S;
+    rt[2] = thr_out;
+    rt[3] = thr_in;
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      if (q >= k) break;
+      reinterpret_cast<int*>(rt)[4 + q] = sel_i[q];
+      rt[12 + q] = gt[q];
+      if (t < T) {
+        a.topk_idx[t * k + q] = sel_i[q];
+        a.topk_gate[t * k + q] = gt[q];
+      }
+    }
+  };
+
+  // phase 2 (wave 0), lane = token: merge the 8 sorted lists and certify the
+  // token; certified tokens get their results, the others return false
+  auto merge = [&]() -> bool {
+    const int64_t t = t0 + lane;
+    float sel_v[KK];
+    int sel_i[KK];
+    uint32_t heads = 0;  // 4 bits per list: index of its next candidate
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
+      float best = -INFINITY;
+      int bi = 0x7FFFFFFF, bw = -1;
+      for (int w = 0; w < 8; ++w) {
+        const int hd = (int)((heads >> (4 * w)) & 15u);
+        if (hd >= KK) continue;
+        const float v = cand_v[(w * KK + hd) * 64 + lane];
+        const int i = cand_i[(w * KK + hd) * 64 + lane];
+        if (i == 0x7FFFFFFF) continue;
+        if (bw < 0 || better(v, i, best, bi)) {
+          best = v;
+          bi = i;
+          bw = w;
+        }
+      }
+      if (bw >= 0) heads += 1u << (4 * bw);
+      sel_v[r] = best;
+      sel_i[r] = bi;
+    }
+    if (t >= T) return true;  // rows past T: nothing to route
+    bool ok = !a.force_fallback;
+    const float b2 = 2.0f * bmax_s[lane];
+    const int ngap = min(k, KK - 1);
+#pragma unroll
+    for (int r = 0; r + 1 < KK; ++r)
+      if (r < ngap) ok = ok && (sel_v[r] - sel_v[r + 1] > b2);  // false for NaN
+    if (!ok) return false;
+    float m = -INFINITY;
+    for (int w = 0; w < 8; ++w) m = fmaxf(m, wmax[w * 64 + lane]);
+    float S = 0.0f;
+    for (int w = 0; w < 8; ++w) {
+      const float mw = wmax[w * 64 + lane];
+      if (mw != -INFINITY) S += wsum[w * 64 + lane] * fast_exp(mw - m);
+    }
+    finish(lane, sel_v, sel_i, m, S);
+    return true;
+  };
+
+  // one wave, lane = expert (e = lane + 64 c): top-KK and softmax of token tl
+  // from its canonical logits in H (repeated wave arg-max, value desc, index asc)
+  auto reselect = [&](int tl) {
+    constexpr int G = EP / 64;
+    const float* hrow = Hs + tl * HS;
+    float hv[G];
+#pragma unroll
+    for (int c = 0; c < G; ++c) hv[c] = lane + 64 * c < E ? hrow[lane + 64 * c] : -INFINITY;
+    uint32_t taken = 0;
+    float sel_v[KK];
+    int sel_i[KK];
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
+      float v = -INFINITY;
+      int i = 0x7FFFFFFF;
+#pragma unroll
+      for (int c = 0; c < G; ++c)
+        if (lane + 64 * c < E && !((taken >> c) & 1u) && better(hv[c], lane + 64 * c, v, i)) {
+          v = hv[c];
+          i = lane + 64 * c;
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(v, off);
+        const int oi = __shfl_xor(i, off);
+        if (better(ov, oi, v, i)) {
+          v = ov;
+          i = oi;
+        }
+      }
+      sel_v[r] = v;
+      sel_i[r] = i;
+      if (i != 0x7FFFFFFF && (i & 63) == lane) taken |= 1u << (i >> 6);
+    }
+    const float m = sel_v[0];
+    float S = 0.0f;
+#pragma unroll
+    for (int c = 0; c < G; ++c)
+      if (lane + 64 * c < E) S += fast_exp(hv[c] - m);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+    if (lane == 0) finish(tl, sel_v, sel_i, m, S);
+  };
+
+
+  scan();
+  __syncthreads();
+  if (wave == 0) {
+    const bool ok = merge();
+    const uint64_t bad = __ballot(!ok);
+    if (!ok) flist_s[__builtin_amdgcn_mbcnt_hi((uint32_t)(bad >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bad, 0u))] = lane;
+    if (lane == 0) nflag_s = __popcll(bad);
+  }
+  __syncthreads();
+
+  // ---- fallback: canonical fp32 chains for the uncertified tokens ------------------
+  // Rounds of 16 flagged tokens. Thread (slot f0, column c) of TPR x NCOL runs
+  // the chains of tokens f0*NFG .. +NFG for column c; weight tiles and the
+  // tokens' x chunks stream through a 2-stage LDS ring (direct-to-LDS loads).
+  const int nflag = nflag_s;
+  if (nflag > 0) {
+    constexpr int TPR = 512 / NCOL;  // token slots
+    constexpr int NFG = FR / TPR;    // tokens per thread
+    const int f0 = tid / NCOL, c = tid % NCOL;
+    const int32x4 rsXall = buffer_rsrc(a.x, (uint32_t)(T * d * 2));
+    const uint32_t fl0 = lds_address(&smem_u4[OFF_CV / 16]);
+    uint32_t fvoff[F_NR];  // byte offsets (x offsets can pass 2^31; T*d*2 < 2^32 is checked on the host)
+    bool fisW[F_NR], fact[F_NR];
+    int fld = 0;
+#pragma unroll
+    for (int i = 0; i < F_NR; ++i) {
+      fact[i] = (i * 512 + wave * 64) < F_CH;  // wave-uniform (the x chunks may fill part of a wave)
+      fisW[i] = (i * 512 + wave * 64) < F_WCH;
+      fld += fact[i] ? 1 : 0;
+      const int cc = tid + 512 * i;
+      const int kr = cc / BCR, p = cc % BCR;
+      fvoff[i] = (uint32_t)(kr * NCOL * 2 + ((p ^ swz_w<BCR>(kr)) << 4));  // weight chunks (x chunks set per round)
+    }
+    // One round: NF tokens per thread (TPR * NF tokens), chains interleaved over
+    // the tokens so consecutive fmas are independent.
+    auto round = [&](int base, auto nf_tag) {
+      constexpr int NF = decltype(nf_tag)::value;
+      constexpr int RT = TPR * NF;  // tokens in this round
+      // x chunk slots: row r of the round (token flist[base + r], or a valid row), chunk p
+#pragma unroll
+      for (int i = 0; i < F_NR; ++i) {
+        const int cc = tid + 512 * i - F_WCH;
+        if (cc >= 0) {
+          const int r = min(cc / F_CPR, FR - 1), p = cc % F_CPR;  // lanes past the x chunks: any valid offset
+          const int m = flist_s[min(base + r, nflag - 1)];
+          fvoff[i] = (uint32_t)((t0 + m) * d * 2) + (uint32_t)(p << 4);
+        }
+      }
+      auto fissue = [&](int kt) {
+        const int st = kt % F_STAGES;
+#pragma unroll
+        for (int i = 0; i < F_NR; ++i) {
+          if (!fact[i]) continue;
+          const uint32_t dst = fl0 + (uint32_t)((st * F_CH + i * 512 + wave * 64) * 16);
+          if (fisW[i]) {
+            load_to_lds(__builtin_amdgcn_readfirstlane(dst), (int)(fvoff[i] + (uint32_t)(kt * F_BK * NCOL * 2)), rsW, 0);
+          } else if (tid + 512 * i < F_WCH + RT * F_CPR) {  // x chunks of this round's rows
+            load_to_lds(__builtin_amdgcn_readfirstlane(dst), (int)(fvoff[i] + (uint32_t)(kt * F_BK * 2)), rsXall, 0);
+          }
+        }
+      };
+      float accv[NF];
+#pragma unroll
+      for (int q = 0; q < NF; ++q) accv[q] = 0.0f;
+      const int fnk = (d + F_BK - 1) / F_BK;
+#pragma unroll
+      for (int t = 0; t < F_STAGES - 1; ++t)
+        if (t < fnk) fissue(t);
+      for (int kt = 0; kt < fnk; ++kt) {
+        wait_stages<F_STAGES - 2>(fld, min(F_STAGES - 2, fnk - 1 - kt));
+        block_barrier();  // stage kt in LDS for every wave; the buffer of stage kt-1 is free
+        if (kt + F_STAGES - 1 < fnk) fissue(kt + F_STAGES - 1);
+        const char* sb = smem + OFF_CV + (kt % F_STAGES) * F_CH * 16;
+        const uint16_t* sw = reinterpret_cast<const uint16_t*>(sb);
+        const uint4* sx = reinterpret_cast<const uint4*>(sb + F_WCH * 16);
+        const int nj = min(F_BK, d - kt * F_BK);  // a multiple of 8
+        auto do_q8 = [&](int q8) {
+          float wv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int jj = q8 * 8 + u;
+            wv[u] = bf16_to_f32(sw[jj * NCOL + (((c >> 3) ^ swz_w<BCR>(jj)) << 3) + (c & 7)]);
+          }
+          uint4 xv[NF];
+#pragma unroll
+          for (int q = 0; q < NF; ++q) xv[q] = sx[(f0 * NF + q) * F_CPR + q8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int q = 0; q < NF; ++q) {
+              const uint32_t w2 = (&xv[q].x)[u >> 1];
+              const float xs = (u & 1) ? bf16_hi(w2) : bf16_lo(w2);
+              accv[q] = __builtin_fmaf(xs, wv[u], accv[q]);
+            }
+        };
+        if (nj == F_BK) {
+#pragma unroll
+          for (int q8 = 0; q8 < F_CPR; ++q8) do_q8(q8);  // full stage: every LDS read can be issued early
+        } else {
+          for (int q8 = 0; q8 < nj / 8; ++q8) do_q8(q8);
+        }
+      }
+      block_barrier();  // the ring is reused by the next round
+#pragma unroll
+      for (int q = 0; q < NF; ++q) {
+        const int fi = base + f0 * NF + q;
+        const bool on = fi < nflag;
+        const int m = flist_s[min(fi, nflag - 1)];
+        const int64_t t = t0 + m;
+        if constexpr (NOISY) {
+          const float accn = __shfl_xor(accv[q], 32);  // column c + 32 holds the same expert's noise logit
+          const int e = 32 * (c >> 6) + (c & 31);
+          if (on && !(c & 32) && e < E) {
+            float cl = accv[q];
+            if (a.bias) cl = cl + a.bias[e];
+            const float sp = canon_softplus(accn);
+            const float h = __builtin_fmaf(a.noise[t * E + e], sp, cl);
+            Hs[m * HS + e] = h;
+            a.CL[t * a.lpad + e] = cl;
+            a.SG[t * a.lpad + e] = sp;
+          }
+        } else {
+          const int e = c;
+          if (on && e < E) {
+            float cl = accv[q];
+            if (a.bias) cl = cl + a.bias[e];
+            Hs[m * HS + e] = cl;
+          }
+        }
+      }
+      return RT;
+    };
+    for (int base = 0; base < nflag;) {
+      const int need = (nflag - base + TPR - 1) / TPR;  // tokens per thread still needed
+      if (need <= 1) base += round(base, std::integral_constant<int, 1>{});
+      else if (need <= 2 || NFG < 4) base += round(base, std::integral_constant<int, (NFG < 2 ? NFG : 2)>{});
+      else if (need <= 4 || NFG < 8) base += round(base, std::integral_constant<int, (NFG < 4 ? NFG : 4)>{});
+      else if (need <= 8 || NFG < 16) base += round(base, std::integral_constant<int, (NFG < 8 ? NFG : 8)>{});
+      else base += round(base, std::integral_constant<int, NFG>{});
+    }
+    __syncthreads();
+    for (int q = wave; q < nflag; q += 8) reselect(flist_s[q]);
+    __syncthreads();
+  }
+
+  // ---- phase 3, lane = expert: sums over token slices in token order ---------------
+  constexpr int G = EP / 64;   // expert groups of 64
+  constexpr int TS = 8 / G;    // token slices
+  constexpr int TL = kTok / TS;
+  const int gq = wave % G, ts = wave / G;
+  const int e = gq * 64 + lane;
+  if (e < E) {
+    const bool have_in = KK > k;
+    const int tl_lo = min(rows, ts * TL), tl_hi = min(rows, tl_lo + TL);
+    float p_sum = 0.0f, imp_sum = 0.0f, ld_sum = 0.0f;
+    int cnt = 0;
+    constexpr int TB = 8;  // tokens whose global loads are in flight together
+    for (int tb = tl_lo; tb < tl_hi; tb += TB) {
+      float cb[TB], sb[TB];
+      if constexpr (NOISY) {
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+          const int64_t t = t0 + min(tb + u, tl_hi - 1);
+          cb[u] = a.CL[t * a.lpad + e];
+          sb[u] = a.SG[t * a.lpad + e];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const int tl = tb + u;
+        if (tl >= tl_hi) break;
+        const float* rt = res + tl * RS;
+        const float h = Hs[tl * HS + e];
+        p_sum += fast_exp(h - rt[0]) * rt[1];
+        bool in_k = false;
+        float gk = 0.0f;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+          if (q >= k) break;
+          if (reinterpret_cast<const int*>(rt)[4 + q] == e) {
+            in_k = true;
+            gk = rt[12 + q];
+          }
+        }
+        imp_sum += gk;
+        cnt += in_k ? 1 : 0;
+        if constexpr (NOISY) {
+          const float thr = in_k ? rt[3] : rt[2];
+          ld_sum += (in_k && !have_in) ? 1.0f : fast_normal_cdf((cb[u] - thr) * __builtin_amdgcn_rcpf(sb[u]));
+        }
+      }
+    }
+    const int o = ts * EP + e;
+    part[0 * 512 + o] = p_sum;
+    part[1 * 512 + o] = imp_sum;
+    part[2 * 512 + o] = ld_sum;
+    reinterpret_cast<int*>(part)[3 * 512 + o] = cnt;
+  }
+  __syncthreads();
+  if (tid < E) {
+    float p_sum = 0.0f, imp_sum = 0.0f, ld_sum = 0.0f;
+    int cnt = 0;
+    for (int q = 0; q < TS; ++q) {
+      const int o = q * EP + tid;
+      p_sum += part[0 * 512 + o];
+      imp_sum += part[1 * 512 + o];
+      ld_sum += part[2 * 512 + o];
+      cnt += reinterpret_cast<const int*>(part)[3 * 512 + o];
+    }
+    const int64_t o = (int64_t)tid * a.nblk + blockIdx.x;
+    a.part_prob[o] = p_sum;
+    a.part_imp[o] = imp_sum;
+    a.part_load[o] = ld_sum;
+    a.part_cnt[o] = cnt;
+  }
+}
+
+template <int EP, bool NOISY, int KK>
+hipError_t launch_fused_t(const FusedArgs& fa, hipStream_t s) {
+  hipLaunchKernelGGL((route_fused_kernel<EP, NOISY, KK>), dim3((unsigned)fa.nblk), dim3(512), 0, s, fa);
+  return hipGetLastError();
+}
+
+template <int EP, bool NOISY>
+hipError_t launch_fused_kk(int kk, const FusedArgs& fa, hipStream_t s) {
+  switch (kk) {
+    case 1: return launch_fused_t<EP, NOISY, 1>(fa, s);
+    case 2: return launch_fused_t<EP, NOISY, 2>(fa, s);
+    case 3: return launch_fused_t<EP, NOISY, 3>(fa, s);
+    case 4: return launch_fused_t<EP, NOISY, 4>(fa, s);
+    case 5: return launch_fused_t<EP, NOISY, 5>(fa, s);
+    case 6: return launch_fused_t<EP, NOISY, 6>(fa, s);
+    case 7: return launch_fused_t<EP, NOISY, 7>(fa, s);
+    case 8: return launch_fused_t<EP, NOISY, 8>(fa, s);
+    default: return launch_fused_t<EP, NOISY, 9>(fa, s);
+  }
+}
+
+int fused_ep(int E) { return E <= 64 ? 64 : (E <= 128 ? 128 : 256); }
+
+}  // namespace
+}  // namespace moe
+
+bool route_fused_supported(int dtype, int E) { return dtype == 1 && E <= 256; }
+
+size_t route_wcat_elems(int d, int E, bool noisy) {
+  return (size_t)d * moe::fused_ep(E) * (noisy ? 2 : 1);
+}
+
+hipError_t launch_route_fused(const RouteLaunch& a, bool noisy, int force_fallback, float* CL, float* SG, int lpad,
+                              hipStream_t s) {
+  using namespace moe;
+  const int EP = fused_ep(a.E);
+  const int ncol = EP * (noisy ? 2 : 1);
+  const int64_t n = (int64_t)a.d * ncol;
+  hipLaunchKernelGGL(route_wcat_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(a.w_gate), static_cast<const uint16_t*>(noisy ? a.w_noise : nullptr),
+                     a.wcat, a.d, a.E, ncol);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  FusedArgs fa;
+  fa.T = a.T;
+  fa.d = a.d;
+  fa.E = a.E;
+  fa.k = a.k;
+  fa.renormalize = a.renormalize;
+  fa.nblk = (int)((a.T + kTok - 1) / kTok);
+  fa.force_fallback = force_fallback;
+  fa.lpad = lpad;
+  fa.x = static_cast<const uint16_t*>(a.x);
+  fa.wcat = a.wcat;
+  fa.bias = a.gate_bias;
+  fa.noise = a.noise;
+  fa.topk_idx = a.topk_idx;
+  fa.topk_gate = a.topk_gate;
+  fa.CL = CL;
+  fa.SG = SG;
+  fa.part_prob = a.part_prob;
+  fa.part_imp = a.part_imp;
+  fa.part_load = a.part_load;
+  fa.part_cnt = a.part_cnt;
+  const int kk = a.k + 1 < a.E ? a.k + 1 : a.E;
+  if (EP == 64) return noisy ? launch_fused_kk<64, true>(kk, fa, s) : launch_fused_kk<64, false>(kk, fa, s);
+  if (EP == 128) return noisy ? launch_fused_kk<128, true>(kk, fa, s) : launch_fused_kk<128, false>(kk, fa, s);
+  return noisy ? launch_fused_kk<256, true>(kk, fa, s) : launch_fused_kk<256, false>(kk, fa, s);
+}

@@ -5,7 +5,9 @@ Comparison rules (tolerances from the layer's numerics contract):
 * integer outputs (expert ids, counts, offsets, slots, row sources) and the
   permuted copy x_perm: bit-exact;
 * gate logits H: bit-exact (both sides evaluate the same fp32 operations);
-* float outputs (gates, FFN rows, y, aux): relative error per tensor
+* gates: absolute error within 1e-5 (fp32 layers) or 1e-4 (bf16 layers, whose
+  certified tokens use gates from the MFMA logits);
+* float outputs (FFN rows, y, aux): relative error per tensor
   ||Y - Y_ref||_F / ||Y_ref||_F and per non-zero row ||Y_t - Y_ref_t|| /
   ||Y_ref_t|| within 2e-2 for bf16 and 1e-5 for fp32; rows whose every slot
   was dropped must be exactly zero.
@@ -20,7 +22,10 @@ import numpy as np
 from synthetic import bf16_bits_to_f32
 
 TOL = {"bf16": 2e-2, "f32": 1e-5}
-GATE_ATOL = 1e-5
+# Gates: fp32 layers (and canonical-logit gates) within 1e-5; bf16 layers take
+# the gates of certified tokens from the MFMA logits, which differ from the
+# canonical ones at the rounding level (|dH| ~ 1e-5), hence 1e-4.
+GATE_ATOL = {"bf16": 1e-4, "f32": 1e-5}
 
 
 def say(msg: str):

@@ -56,10 +56,10 @@ def _case(name, **over):
     return out
 
 
-def _params(moelib, c):
+def _params(moelib, c, gate_mode=0):
     cfg = c["cfg"]
     return moelib.make_params(cfg.T, cfg.d_model, cfg.d_ff, cfg.E, cfg.k, cfg.dtype, cfg.act, cfg.renormalize,
-                              cfg.capacity_factor, c["cap"])
+                              cfg.capacity_factor, c["cap"], gate_mode)
 
 
 def test_canonical_softplus_bitwise(moelib, dev):
@@ -100,7 +100,37 @@ def test_route_full_size(moelib, dev, name):
     assert mism.size == 0, f"{mism.size} logits differ bitwise (first flat index {mism[:3]})"
     assert np.array_equal(to_numpy(b.topk_idx), r["topk_idx"])
     assert np.array_equal(to_numpy(b.counts_routed), r["counts_routed"])
-    assert np.abs(to_numpy(b.topk_gate) - r["topk_gate"]).max() <= GATE_ATOL
+    assert np.abs(to_numpy(b.topk_gate) - r["topk_gate"]).max() <= GATE_ATOL["f32"]
+    aux_ok(to_numpy(b.aux), r["aux"], 1e-4)
+
+
+MODES = {"auto": 0, "canonical": 1, "fallback": 2}
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("name", FULL)
+def test_route_gate_modes_full_size(moelib, dev, name, mode):
+    """Without logits_out the bf16 layers (E <= 256) route through the
+    certified MFMA gate; every mode must give the canonical routing."""
+    import torch
+    from sparsely_gated_mixture_gate_amd.buffers import StepBuffers, to_numpy
+
+    c = _case(name)
+    cfg, r, d = c["cfg"], c["route"], c["dev"]
+    p = _params(moelib, c, MODES[mode])
+    b = StepBuffers.alloc(p, dev)
+    say(f"[route-{mode}] {cfg.name}")
+    moelib.moe_route(p, d["x"], d["w_gate"], d["gate_bias"], d["w_noise"], d["noise"], b.topk_idx, b.topk_gate,
+                     b.counts_routed, b.aux, None, b.ws_route)
+    torch.cuda.synchronize()
+    idx = to_numpy(b.topk_idx)
+    bad = np.flatnonzero((idx != r["topk_idx"]).any(axis=1))
+    assert bad.size == 0, f"{bad.size} tokens routed differently, e.g. {bad[:5]}: {idx[bad[:3]]} vs {r['topk_idx'][bad[:3]]}"
+    assert np.array_equal(to_numpy(b.counts_routed), r["counts_routed"])
+    tol = GATE_ATOL["f32"] if mode != "auto" else GATE_ATOL[cfg.dtype]
+    gerr = np.abs(to_numpy(b.topk_gate) - r["topk_gate"]).max()
+    say(f"  max gate error {gerr:.2e}")
+    assert gerr <= tol
     aux_ok(to_numpy(b.aux), r["aux"], 1e-4)
 
 
@@ -172,12 +202,12 @@ def test_combine_full_size(moelib, dev, name):
     rel_rows_ok(as_f64(to_numpy(b.y), cfg.dtype), ref, TOL[cfg.dtype], f"y {cfg.name}")
 
 
-def _run_forward(moelib, c, dev):
+def _run_forward(moelib, c, dev, gate_mode=0):
     import torch
     from sparsely_gated_mixture_gate_amd.buffers import ForwardBuffers
 
     d = c["dev"]
-    p = _params(moelib, c)
+    p = _params(moelib, c, gate_mode)
     fb = ForwardBuffers.alloc(p, dev)
     moelib.moe_forward(p, d["x"], d["w_gate"], d["gate_bias"], d["w_noise"], d["noise"], d["w1"], d["w2"], fb.y,
                        fb.aux, fb.topk_idx, fb.topk_gate, fb.counts_routed, fb.counts_kept, fb.slot_dest, fb.ws)
@@ -193,7 +223,7 @@ def _check_forward(c, fb, tokens):
     assert np.array_equal(to_numpy(fb.counts_routed), r["counts_routed"])
     assert np.array_equal(to_numpy(fb.counts_kept), disp["counts_kept"])
     assert np.array_equal(to_numpy(fb.slot_dest), disp["slot_dest"])
-    assert np.abs(to_numpy(fb.topk_gate) - r["topk_gate"]).max(initial=0.0) <= GATE_ATOL
+    assert np.abs(to_numpy(fb.topk_gate) - r["topk_gate"]).max(initial=0.0) <= GATE_ATOL[cfg.dtype]
     aux_ok(to_numpy(fb.aux), r["aux"], 1e-4)
     ref = oracle.forward(c["spec"], c["inp"], tokens=tokens)
     got = as_f64(to_numpy(fb.y)[tokens], cfg.dtype)
@@ -232,11 +262,12 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("mode", ["auto", "fallback"])
 @pytest.mark.parametrize("name,over", SMALL, ids=[f"{n}-{'-'.join(f'{k}{v}' for k, v in o.items())}" for n, o in SMALL])
-def test_forward_small_shapes(moelib, dev, name, over):
+def test_forward_small_shapes(moelib, dev, name, over, mode):
     c = _case(name, **over)
-    say(f"[forward-small] {c['cfg'].name} C={c['C']}")
-    fb = _run_forward(moelib, c, dev)
+    say(f"[forward-small-{mode}] {c['cfg'].name} C={c['C']}")
+    fb = _run_forward(moelib, c, dev, MODES[mode])
     _check_forward(c, fb, np.arange(c["cfg"].T))
 
 
