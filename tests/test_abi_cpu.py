@@ -69,6 +69,8 @@ def test_workspace_sizes(moelib):
     (dict(d_ff=0), "MOE_ERR_INVALID_ARG"),
     (dict(T=-1), "MOE_ERR_INVALID_ARG"),
     (dict(T=2**30, k=2), "MOE_ERR_UNSUPPORTED"),
+    (dict(gate_mode=3), "MOE_ERR_INVALID_ARG"),
+    (dict(gate_mode=-1), "MOE_ERR_INVALID_ARG"),
 ])
 def test_invalid_params_rejected(moelib, kw, status):
     with pytest.raises(moelib.MoEError) as ei:
