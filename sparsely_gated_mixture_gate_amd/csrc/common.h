@@ -12,14 +12,12 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16, round to nearest, ties to even (inputs are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest, ties to even:
+// one v_cvt_pk_bf16_f32 on gfx950 (the default round mode is nearest-even).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Activation of the first expert layer: ReLU, or the exact GELU 0.5 z (1 + erf(z / sqrt 2)).
@@ -108,6 +106,8 @@ struct DispatchLaunch {
   int32_t* row_src;
   void* x_perm;
   int32_t* blk_cnt;  // [E][nb] workspace
+  int32_t* tile_start;  // [E+1] M-tile prefix for the expert FFN, or null
+  int tile_rows;        // M-tile rows of that prefix
 };
 int64_t dispatch_num_blocks(int64_t assignments);
 hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s);
@@ -123,8 +123,10 @@ struct FfnLaunch {
   void* y_perm;
   void* h1;             // [max_rows, f] dtype workspace
   int32_t* tile_start;  // [E+1] workspace
+  bool tile_map_ready;  // tile_start already holds the M-tile prefix (built by the dispatch scan)
 };
 hipError_t launch_expert_ffn(const FfnLaunch& a, hipStream_t s);
+int ffn_tile_rows(int dtype, int64_t capacity, int64_t max_rows, int E);  // M-tile rows the FFN launch uses
 
 struct CombineLaunch {
   int64_t T;

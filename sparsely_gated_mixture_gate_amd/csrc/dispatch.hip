@@ -41,7 +41,8 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
 
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ blk_cnt, int nb, int E,
                                                              int64_t C, int32_t* __restrict__ counts_kept,
-                                                             int32_t* __restrict__ offsets) {
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ tile_start, int tile_rows) {
   __shared__ int64_t sc[1024];
   const int e = threadIdx.x;
   int64_t run = 0;
@@ -65,6 +66,20 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
   }
   if (e < E) offsets[e] = (int32_t)(sc[e] - kept);
   if (e == E - 1) offsets[E] = (int32_t)sc[e];
+  if (!tile_start) return;
+  // prefix of ceil(kept / tile_rows) M-tiles per expert for the expert FFN
+  const int64_t tiles = (kept + tile_rows - 1) / tile_rows;
+  __syncthreads();
+  sc[e] = tiles;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int64_t v = e >= off ? sc[e - off] : 0;
+    __syncthreads();
+    sc[e] += v;
+    __syncthreads();
+  }
+  if (e < E) tile_start[e] = (int32_t)(sc[e] - tiles);
+  if (e == E - 1) tile_start[E] = (int32_t)sc[e];
 }
 
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __restrict__ idx, int64_t n, int k,
@@ -145,7 +160,7 @@ hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, a.blk_cnt, nb, a.E, a.C, a.counts_kept,
-                     a.offsets);
+                     a.offsets, a.tile_start, a.tile_rows);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (nb == 0) return hipSuccess;
   int nbits = 0;

@@ -13,18 +13,23 @@
 //     ceil(rows_e / BM) M-tiles per expert; GEMM blocks binary-search it, so the
 //     host never synchronises on the ragged segment sizes. The grid is an upper
 //     bound (ceil(R_max / BM) + E M-tiles); surplus blocks exit at once.
-//   * bf16 path: BM x 256 x 64 tiles (BM = 128 for experts of about one tile of
-//     rows, where the weights stream from HBM; 256 for large segments, where the
-//     MFMAs bound), 512 threads = 2 x 4 waves, MFMA v_mfma_f32_16x16x32_bf16 with
-//     fp32 accumulation. Both operands are copied to LDS in their HBM layout
-//     (16-byte chunks, XOR-swizzled per row against bank conflicts): activation
-//     rows K-contiguous, read as one ds_read_b128 per MFMA operand; weight rows
-//     N-contiguous, read K-contiguous with the gfx950 transposing load
-//     ds_read_b64_tr_b16 (two per operand). Double-buffered LDS with the next
-//     tiles' global loads in flight (register staging two k-tiles ahead). The MFMA runs with swapped
-//     operands (D = W^T A^T) so each lane ends with 4 consecutive output columns
-//     of a row (8-byte stores); ReLU / GELU is applied in fp32 before the bf16
-//     (nearest-even) store, GELU with a branch-free erf accurate to 1.5e-7.
+//   * bf16 path: BM x 256 x BK tiles, 512 threads = 2 x 4 waves of
+//     (BM/2) x 64, MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation. Tile
+//     shape by the rows an expert can hold: capacity <= 160 -> 160 x 256 x 64
+//     (3 stages), capacity <= 256 -> 256 x 256 x 32 (4 stages), both one M-tile
+//     per expert with 16-row MFMA tiles past the segment skipped and their A rows
+//     loaded as zero; otherwise about one tile of rows per expert -> 128 x 256 x 64
+//     (3 stages), large segments -> 256 x 256 x 32 (4 stages). Both operands go
+//     HBM -> LDS in their HBM layout by direct-to-LDS buffer loads (16-byte
+//     chunks, XOR-swizzled per row against bank conflicts) into an NSTAGE-deep
+//     ring, NSTAGE - 1 k-tiles in flight, explicit vmcnt waits and a fence-free
+//     barrier; activation rows (K-contiguous) are read with ds_read_b128,
+//     weight rows (N-contiguous) K-contiguous with the gfx950 transposing read
+//     ds_read_b64_tr_b16 (two per operand). The MFMA runs with swapped operands
+//     (D = W^T A^T) so each lane ends with 4 consecutive output columns of a
+//     row (8-byte stores); ReLU / GELU is applied in fp32 before the bf16
+//     (nearest-even, v_cvt_pk_bf16_f32) store, GELU with a branch-free erf
+//     accurate to 1.5e-7.
 //   * scheduling: real tiles are dealt evenly to the 8 XCDs in contiguous
 //     chunks (tiles sharing an activation or weight panel share that XCD's L2),
 //     rastered inside each expert in groups of 4 M-tiles.
@@ -127,32 +132,33 @@ __device__ __forceinline__ int swz_a_rc(int row) {
 }
 
 // C[rows of segment e] = act?(A . W[e]); A [R][K], W [E][K][N], C [R][N], all bf16.
-// BM x BN x BK tiles (BN = 256 or 128), 512 threads = (8 / (BN/64)) x (BN/64)
-// waves of 64 columns each, NSTAGE-deep LDS ring fed by direct-to-LDS buffer
-// loads (NSTAGE - 1 k-tiles in flight).
-template <int BM, int BN, int BK, int NSTAGE, int ACT, bool APPLY_ACT, bool SKIP>
-__global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A,
+// BM x BN x BK tiles (BN = 256 or 128), NW waves (64 NW threads) of WNT
+// columns each, (NW / (BN/WNT)) x (BN/WNT); NSTAGE-deep LDS ring fed by
+// direct-to-LDS buffer loads (NSTAGE - 1 k-tiles in flight).
+template <int BM, int BN, int BK, int NSTAGE, int ACT, bool APPLY_ACT, bool SKIP, int NW, int WNT>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                                 const uint16_t* __restrict__ W,
                                                                 uint16_t* __restrict__ C,
                                                                 const int32_t* __restrict__ offsets,
                                                                 const int32_t* __restrict__ tile_start, int E,
                                                                 int K, int N, int n_tiles_n) {
-  constexpr int WN_W = BN / 64;          // waves along N
-  constexpr int WM_W = 8 / WN_W;         // waves along M
+  constexpr int NT = 64 * NW;            // threads
+  constexpr int WN_W = BN / WNT;         // waves along N
+  constexpr int WM_W = NW / WN_W;        // waves along M
   constexpr int BCR = BN / 8;            // 16-byte chunks per B row
   constexpr int WM = BM / WM_W;          // wave tile rows
   constexpr int MI = WM / 16;            // 16-row MFMA tiles per wave
-  constexpr int NI = 4;                  // 16-column MFMA tiles per wave (64 columns)
+  constexpr int NI = WNT / 16;           // 16-column MFMA tiles per wave
   constexpr int RC = BK / 8;             // 16-byte chunks per A row
   constexpr int A_CH = BM * RC;          // chunks per A tile
   constexpr int B_CH = BK * BCR;         // chunks per B tile
-  constexpr int A_LD = (A_CH + 511) / 512;  // A loads per thread per tile (the last round may be partial)
-  constexpr int A_TAIL_W = (A_CH % 512) / 64;  // waves that issue the partial last round (0: none)
-  constexpr int B_LD = B_CH / 512;
+  constexpr int A_LD = (A_CH + NT - 1) / NT;  // A loads per thread per tile (the last round may be partial)
+  constexpr int A_TAIL_W = (A_CH % NT) / 64;  // waves that issue the partial last round (0: none)
+  constexpr int B_LD = B_CH / NT;
   constexpr int LD_HI = A_LD + B_LD;                       // loads per tile of waves < A_TAIL_W
   constexpr int LD_LO = A_LD - (A_TAIL_W ? 1 : 0) + B_LD;  // loads per tile of the other waves
   constexpr int STAGE_CH = A_CH + B_CH;
-  static_assert(A_CH % 64 == 0 && B_CH % 512 == 0, "tile / thread mismatch");
+  static_assert(A_CH % 64 == 0 && B_CH % NT == 0 && WN_W * WM_W == NW, "tile / thread mismatch");
   static_assert(NSTAGE >= 2 && NSTAGE <= 5, "stages");
   static_assert((BN == 128 || BN == 256) && WM % 16 == 0, "tile shape");
   __shared__ uint4 smem[NSTAGE * STAGE_CH];
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
   int voffA[A_LD], voffA_last[A_LD], voffB[B_LD], voffB_last[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int c = tid + 512 * i;
+    const int c = tid + NT * i;
     const int row = c / RC, phys = c % RC;
     const int kc = phys ^ swz_a_rc<RC>(row);
     const int lrow = min(row, rows - 1);
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int c = tid + 512 * i;
+    const int c = tid + NT * i;
     const int kr = c / BCR, phys = c % BCR;
     const int nc = phys ^ (2 * swz_b(kr));
     const int gn = n0 + nc * 8;
@@ -207,12 +213,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
       if (A_TAIL_W && i == A_LD - 1 && wave >= A_TAIL_W) break;
-      const uint32_t dst = lds0 + (uint32_t)((st * STAGE_CH + i * 512 + wave * 64) * 16);
+      const uint32_t dst = lds0 + (uint32_t)((st * STAGE_CH + i * NT + wave * 64) * 16);
       load_to_lds(__builtin_amdgcn_readfirstlane(dst), last ? voffA_last[i] : voffA[i], rsA, soffA);
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const uint32_t dst = lds0 + (uint32_t)((st * STAGE_CH + A_CH + i * 512 + wave * 64) * 16);
+      const uint32_t dst = lds0 + (uint32_t)((st * STAGE_CH + A_CH + i * NT + wave * 64) * 16);
       load_to_lds(__builtin_amdgcn_readfirstlane(dst), last ? voffB_last[i] : voffB[i], rsB, soffB);
     }
   };
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const int krow = ks * 32 + 8 * g + (s >> 2);
-        const int ncol = wn * 64 + ni * 16 + 4 * (s & 3);
+        const int ncol = wn * WNT + ni * 16 + 4 * (s & 3);
         const int c = ncol >> 3;
         const int b0 = krow * (BN * 2) + ((c ^ (2 * swz_b(krow))) << 4) + ((ncol & 7) << 1);
         const int b1 = (krow + 4) * (BN * 2) + ((c ^ (2 * swz_b(krow + 4))) << 4) + ((ncol & 7) << 1);
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(const uint16_t* 
     if (grow >= row_end) continue;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      const int gcol = n0 + wn * 64 + ni * 16 + 4 * g;
+      const int gcol = n0 + wn * WNT + ni * 16 + 4 * g;
       if (gcol >= N) continue;
       float v[4];
 #pragma unroll
@@ -361,20 +367,21 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 // Grid rounded up to a multiple of the XCD count (surplus workgroups exit at once).
 dim3 grid_for(int64_t tiles) { return dim3((unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds)); }
 
-template <int BM, int BK, int NSTAGE, int ACT, bool SKIP>
+template <int BM, int BK, int NSTAGE, int ACT, bool SKIP, int NW = 8, int WNT = 64, int BN = 256>
 hipError_t launch_bf16(const FfnLaunch& a, hipStream_t s) {
-  constexpr int BN = 256;
-  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, BM, a.tile_start);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (!a.tile_map_ready) {
+    hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, BM, a.tile_start);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   const int64_t mtiles = (a.max_rows + BM - 1) / BM + a.E;
   const int nt1 = (a.f + BN - 1) / BN, nt2 = (a.d + BN - 1) / BN;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, true, SKIP>), grid_for(mtiles * nt1),
-                     dim3(512), 0, s, static_cast<const uint16_t*>(a.x_perm), static_cast<const uint16_t*>(a.w1),
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, true, SKIP, NW, WNT>), grid_for(mtiles * nt1),
+                     dim3(64 * NW), 0, s, static_cast<const uint16_t*>(a.x_perm), static_cast<const uint16_t*>(a.w1),
                      static_cast<uint16_t*>(a.h1), a.offsets, a.tile_start, a.E, a.d, a.f, nt1);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, false, SKIP>), grid_for(mtiles * nt2),
-                     dim3(512), 0, s, static_cast<const uint16_t*>(a.h1), static_cast<const uint16_t*>(a.w2),
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, false, SKIP, NW, WNT>), grid_for(mtiles * nt2),
+                     dim3(64 * NW), 0, s, static_cast<const uint16_t*>(a.h1), static_cast<const uint16_t*>(a.w2),
                      static_cast<uint16_t*>(a.y_perm), a.offsets, a.tile_start, a.E, a.f, a.d, nt2);
   return hipGetLastError();
 }
@@ -382,9 +389,11 @@ hipError_t launch_bf16(const FfnLaunch& a, hipStream_t s) {
 template <int ACT>
 hipError_t launch_f32(const FfnLaunch& a, hipStream_t s) {
   constexpr int TB = 64;
-  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, TB, a.tile_start);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (!a.tile_map_ready) {
+    hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, TB, a.tile_start);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   const int64_t mtiles = (a.max_rows + TB - 1) / TB + a.E;
   const int nt1 = (a.f + TB - 1) / TB, nt2 = (a.d + TB - 1) / TB;
   hipLaunchKernelGGL((grouped_gemm_f32_kernel<ACT, true>), dim3((unsigned)(mtiles * nt1)), dim3(256), 0, s,
@@ -397,23 +406,44 @@ hipError_t launch_f32(const FfnLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int ACT>
-hipError_t launch_ffn_act(const FfnLaunch& a, hipStream_t s) {
-  if (a.dtype != 1) return launch_f32<ACT>(a, s);
+// Tile configuration of a layer, from what the host knows: the dtype, the
+// capacity and the expected rows per expert.
+enum FfnTiles { kTilesF32, kTiles160Skip, kTiles256Skip, kTiles256, kTiles128 };
+FfnTiles ffn_tiles(int dtype, int64_t capacity, int64_t max_rows, int E) {
+  if (dtype != 1) return kTilesF32;
   // A capacity of at most 160 (256) rows puts every expert in one 160-row
   // (256-row) M-tile, so each weight panel is streamed once; MFMA tiles past the
   // segment are skipped.
-  if (a.capacity >= 0 && a.capacity <= 160) return launch_bf16<160, 64, 3, ACT, true>(a, s);
-  if (a.capacity >= 0 && a.capacity <= 256) return launch_bf16<256, 32, 4, ACT, true>(a, s);
+  if (capacity >= 0 && capacity <= 160) return kTiles160Skip;
+  if (capacity >= 0 && capacity <= 256) return kTiles256Skip;
   // Otherwise the expected rows per expert decide the M tile: weight-streaming
   // experts (about one tile of rows each) take 128-row tiles, large segments 256.
-  const int64_t rows_per_expert = a.max_rows / a.E;
-  if (rows_per_expert >= 512) return launch_bf16<256, 32, 4, ACT, false>(a, s);
-  return launch_bf16<128, 64, 3, ACT, false>(a, s);
+  return max_rows / E >= 512 ? kTiles256 : kTiles128;
+}
+
+template <int ACT>
+hipError_t launch_ffn_act(const FfnLaunch& a, hipStream_t s) {
+  switch (ffn_tiles(a.dtype, a.capacity, a.max_rows, a.E)) {
+    case kTilesF32: return launch_f32<ACT>(a, s);
+    case kTiles160Skip: return launch_bf16<160, 64, 3, ACT, true>(a, s);
+    case kTiles256Skip: return launch_bf16<256, 32, 4, ACT, true>(a, s);
+    case kTiles256: return launch_bf16<256, 32, 4, ACT, false>(a, s);
+    default: return launch_bf16<128, 64, 3, ACT, false>(a, s);
+  }
 }
 
 }  // namespace
 }  // namespace moe
+
+int ffn_tile_rows(int dtype, int64_t capacity, int64_t max_rows, int E) {
+  using namespace moe;
+  switch (ffn_tiles(dtype, capacity, max_rows, E)) {
+    case kTilesF32: return 64;
+    case kTiles160Skip: return 160;
+    case kTiles128: return 128;
+    default: return 256;
+  }
+}
 
 hipError_t launch_expert_ffn(const FfnLaunch& a, hipStream_t s) {
   if (a.max_rows <= 0) return hipSuccess;

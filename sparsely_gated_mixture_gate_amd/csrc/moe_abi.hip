@@ -235,7 +235,7 @@ moe_status run_route(const moe_params* p, const void* x, const void* w_gate, con
 
 moe_status run_dispatch(const moe_params* p, const void* x, const int32_t* topk_idx, int32_t* counts_kept,
                         int32_t* offsets, int32_t* slot_dest, int32_t* row_src, void* x_perm, int32_t* blk_cnt,
-                        hipStream_t s) {
+                        int32_t* tile_start, hipStream_t s) {
   DispatchLaunch a;
   a.T = p->T;
   a.d = p->d_model;
@@ -252,12 +252,14 @@ moe_status run_dispatch(const moe_params* p, const void* x, const int32_t* topk_
   a.row_src = row_src;
   a.x_perm = x_perm;
   a.blk_cnt = blk_cnt;
+  a.tile_start = tile_start;
+  a.tile_rows = tile_start ? ffn_tile_rows(p->dtype, capacity_of(p), max_rows_of(p), p->E) : 0;
   const hipError_t e = launch_dispatch(a, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "dispatch launch");
 }
 
 moe_status run_ffn(const moe_params* p, const void* x_perm, const int32_t* offsets, const void* w1, const void* w2,
-                   void* y_perm, const FfnWs& w, hipStream_t s) {
+                   void* y_perm, const FfnWs& w, bool tile_map_ready, hipStream_t s) {
   FfnLaunch a;
   a.d = p->d_model;
   a.f = p->d_ff;
@@ -273,6 +275,7 @@ moe_status run_ffn(const moe_params* p, const void* x_perm, const int32_t* offse
   a.y_perm = y_perm;
   a.h1 = w.h1;
   a.tile_start = w.tile_start;
+  a.tile_map_ready = tile_map_ready;
   const hipError_t e = launch_expert_ffn(a, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "expert FFN launch");
 }
@@ -366,7 +369,7 @@ moe_status moe_dispatch(const moe_params* p, const void* x, const int32_t* topk_
   if ((st = check_ws(p, MOE_OP_DISPATCH, false, ws, ws_bytes)) != MOE_OK) return st;
   Carver c(ws);
   int32_t* blk = carve_dispatch(c, p);
-  return run_dispatch(p, x, topk_idx, counts_kept, offsets, slot_dest, row_src, x_perm, blk,
+  return run_dispatch(p, x, topk_idx, counts_kept, offsets, slot_dest, row_src, x_perm, blk, nullptr,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -384,7 +387,7 @@ moe_status moe_expert_ffn(const moe_params* p, const void* x_perm, const int32_t
   if ((st = check_ws(p, MOE_OP_EXPERT_FFN, false, ws, ws_bytes)) != MOE_OK) return st;
   Carver c(ws);
   const FfnWs w = carve_ffn(c, p);
-  return run_ffn(p, x_perm, offsets, w1, w2, y_perm, w, static_cast<hipStream_t>(stream));
+  return run_ffn(p, x_perm, offsets, w1, w2, y_perm, w, false, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_combine(const moe_params* p, const void* y_perm, const int32_t* slot_dest, const float* topk_gate,
@@ -426,8 +429,10 @@ moe_status moe_forward(const moe_params* p, const void* x, const void* w_gate, c
   if ((st = run_route(p, x, w_gate, gate_bias, w_noise, noise, idx, gate, cr, aux_out, nullptr, w.route, s)) !=
       MOE_OK)
     return st;
-  if ((st = run_dispatch(p, x, idx, ck, w.offsets, sd, w.row_src, w.x_perm, w.blk_cnt, s)) != MOE_OK) return st;
-  if ((st = run_ffn(p, w.x_perm, w.offsets, w1, w2, w.y_perm, w.ffn, s)) != MOE_OK) return st;
+  if ((st = run_dispatch(p, x, idx, ck, w.offsets, sd, w.row_src, w.x_perm, w.blk_cnt, w.ffn.tile_start, s)) !=
+      MOE_OK)
+    return st;
+  if ((st = run_ffn(p, w.x_perm, w.offsets, w1, w2, w.y_perm, w.ffn, true, s)) != MOE_OK) return st;
   return run_combine(p, w.y_perm, sd, gate, y, s);
 }
 

@@ -827,11 +827,16 @@ hipError_t launch_route_fused(const RouteLaunch& a, bool noisy, int force_fallba
   const int EP = fused_ep(a.E);
   const int ncol = EP * (noisy ? 2 : 1);
   const int64_t n = (int64_t)a.d * ncol;
-  hipLaunchKernelGGL(route_wcat_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(a.w_gate), static_cast<const uint16_t*>(noisy ? a.w_noise : nullptr),
-                     a.wcat, a.d, a.E, ncol);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  // a gate-only W_gate [d][E] with E = EP already is the weight layout the kernel reads
+  const uint16_t* wcat = static_cast<const uint16_t*>(a.w_gate);
+  if (noisy || a.E != EP) {
+    hipLaunchKernelGGL(route_wcat_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(a.w_gate),
+                       static_cast<const uint16_t*>(noisy ? a.w_noise : nullptr), a.wcat, a.d, a.E, ncol);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    wcat = a.wcat;
+  }
   FusedArgs fa;
   fa.T = a.T;
   fa.d = a.d;
@@ -842,7 +847,7 @@ hipError_t launch_route_fused(const RouteLaunch& a, bool noisy, int force_fallba
   fa.force_fallback = force_fallback;
   fa.lpad = lpad;
   fa.x = static_cast<const uint16_t*>(a.x);
-  fa.wcat = a.wcat;
+  fa.wcat = wcat;
   fa.bias = a.gate_bias;
   fa.noise = a.noise;
   fa.topk_idx = a.topk_idx;
