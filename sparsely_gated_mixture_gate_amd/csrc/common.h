@@ -32,18 +32,21 @@ __device__ __forceinline__ float activation(float z) {
 
 // GELU for bf16 outputs: erf from Abramowitz & Stegun 7.1.26 (absolute error
 // <= 1.5e-7, far below bf16 rounding), branch-free, with one reciprocal and one
-// exp2. With a = |z|/sqrt 2 and q = P(t) t exp(-a^2), t = 1/(1 + p a),
-// erf(a) = 1 - q, so 1 + erf(z/sqrt 2) = 2 - q for z >= 0 and q for z < 0 (no
-// cancellation for negative z).
+// exp2. With a = |z|/sqrt 2, t = 1/(1 + p a) and q = P(t) t exp(-a^2),
+// erf(a) = 1 - q; then GELU(z) = z Phi(z) = max(z, 0) - h with h = |z| q / 2 for
+// either sign of z (z - h for z >= 0, -h = z q / 2 for z < 0), so there is no
+// cancellation for negative z. The 1/2 is folded into the coefficients of P. |z|
+// is clamped at 10 inside h (h < 1e-20 there), which keeps infinite z finite.
 __device__ __forceinline__ float gelu_fast(float z) {
-  const float a = fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
-  float p = __builtin_fmaf(1.061405429f, t, -1.453152027f);
-  p = __builtin_fmaf(p, t, 1.421413741f);
-  p = __builtin_fmaf(p, t, -0.284496736f);
-  p = __builtin_fmaf(p, t, 0.254829592f);
-  const float q = p * t * __builtin_amdgcn_exp2f(-(a * a) * 1.4426950408889634f);
-  return 0.5f * z * (z >= 0.0f ? 2.0f - q : q);
+  const float za = fminf(fabsf(z), 10.0f);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f * 0.70710678118654752f, za, 1.0f));
+  float r = __builtin_fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
+  r = __builtin_fmaf(r, t, 0.5f * 1.421413741f);
+  r = __builtin_fmaf(r, t, 0.5f * -0.284496736f);
+  r = __builtin_fmaf(r, t, 0.5f * 0.254829592f);
+  r = r * t;
+  const float e = __builtin_amdgcn_exp2f(za * (za * (-0.5f * 1.4426950408889634f)));
+  return __builtin_fmaf(-(za * r), e, fmaxf(z, 0.0f));
 }
 
 template <int ACT>

@@ -23,9 +23,13 @@
 //     HBM -> LDS in their HBM layout by direct-to-LDS buffer loads (16-byte
 //     chunks, XOR-swizzled per row against bank conflicts) into an NSTAGE-deep
 //     ring, NSTAGE - 1 k-tiles in flight, explicit vmcnt waits and a fence-free
-//     barrier; activation rows (K-contiguous) are read with ds_read_b128,
-//     weight rows (N-contiguous) K-contiguous with the gfx950 transposing read
-//     ds_read_b64_tr_b16 (two per operand). The MFMA runs with swapped operands
+//     barrier. For the compute-bound shapes (256-row tiles) the main loop is
+//     software-pipelined: the operands of the next 32-wide k unit are read from
+//     LDS into a second register set between the MFMAs of the current one (one
+//     read per two MFMAs, pinned with scheduling barriers), so the MFMA pipe does
+//     not wait for LDS at each k-tile. Activation rows (K-contiguous) are read
+//     with ds_read_b128, weight rows (N-contiguous) K-contiguous with the gfx950
+//     transposing read ds_read_b64_tr_b16 (two per operand). The MFMA runs with swapped operands
 //     (D = W^T A^T) so each lane ends with 4 consecutive output columns of a
 //     row (8-byte stores); ReLU / GELU is applied in fp32 before the bf16
 //     (nearest-even, v_cvt_pk_bf16_f32) store, GELU with a branch-free erf
@@ -34,8 +38,11 @@
 //     chunks (tiles sharing an activation or weight panel share that XCD's L2),
 //     rastered inside each expert in groups of 4 M-tiles.
 //   * fp32 path: a plain LDS-tiled fp32 FMA kernel (64x64x16 tiles).
+#include <type_traits>
+
 #include "common.h"
 #include "lds_dma.h"
+
 
 namespace moe {
 namespace {
@@ -135,8 +142,8 @@ __device__ __forceinline__ int swz_a_rc(int row) {
 // BM x BN x BK tiles (BN = 256 or 128), NW waves (64 NW threads) of WNT
 // columns each, (NW / (BN/WNT)) x (BN/WNT); NSTAGE-deep LDS ring fed by
 // direct-to-LDS buffer loads (NSTAGE - 1 k-tiles in flight).
-template <int BM, int BN, int BK, int NSTAGE, int ACT, bool APPLY_ACT, bool SKIP, int NW, int WNT>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A,
+template <int BM, int BN, int BK, int NSTAGE, int ACT, bool APPLY_ACT, bool SKIP, int NW, int WNT, bool PF>
+__global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 : 8 / NW) void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                                 const uint16_t* __restrict__ W,
                                                                 uint16_t* __restrict__ C,
                                                                 const int32_t* __restrict__ offsets,
@@ -234,34 +241,39 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void grouped_gemm_bf16_kernel(cons
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](int st) {
+  // A operand (16 rows x 8 k of a 32-wide k step) of MFMA row tile mi from stage st
+  typedef __attribute__((address_space(3))) char lds_char;
+  auto rd_a = [&](int st, int ks, int mi) -> bf16x8 {
     const uint4* sA = &smem[st * STAGE_CH];
-    typedef __attribute__((address_space(3))) char lds_char;
+    const int row = wm * WM + mi * 16 + s;
+    const int ch = ks * 4 + g;
+    return __builtin_bit_cast(bf16x8, sA[row * RC + (ch ^ swz_a_rc<RC>(row))]);
+  };
+  // B operand of MFMA column tile ni. Transposing LDS read: source lane s of each
+  // 16-lane group points at row k0 + s/4, columns n + 4*(s%4) .. +3; lane L of the
+  // group then receives W[k0 .. k0+3][n + L]. Two reads give the 8 k-values.
+  auto rd_b = [&](int st, int ks, int ni) -> bf16x8 {
     lds_char* sB = (lds_char*)(&smem[st * STAGE_CH + A_CH]);
+    const int krow = ks * 32 + 8 * g + (s >> 2);
+    const int ncol = wn * WNT + ni * 16 + 4 * (s & 3);
+    const int c = ncol >> 3;
+    const int b0 = krow * (BN * 2) + ((c ^ (2 * swz_b(krow))) << 4) + ((ncol & 7) << 1);
+    const int b1 = (krow + 4) * (BN * 2) + ((c ^ (2 * swz_b(krow + 4))) << 4) + ((ncol & 7) << 1);
+    const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b0));
+    const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b1));
+    const short __attribute__((ext_vector_type(8))) both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, both);
+  };
+  // all MFMAs of k-tile st, operands read just before use
+  auto compute = [&](int st) {
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       bf16x8 af[MI], bfr[NI];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = wm * WM + mi * 16 + s;
-        const int ch = ks * 4 + g;
-        if (mi < mact) af[mi] = __builtin_bit_cast(bf16x8, sA[row * RC + (ch ^ swz_a_rc<RC>(row))]);
-      }
-      // Transposing LDS read: source lane s of each 16-lane group points at row
-      // k0 + s/4, columns n + 4*(s%4) .. +3; lane L of the group then receives
-      // W[k0 .. k0+3][n + L]. Two reads give the 8 k-values of a bf16 operand.
+      for (int mi = 0; mi < MI; ++mi)
+        if (mi < mact) af[mi] = rd_a(st, ks, mi);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int krow = ks * 32 + 8 * g + (s >> 2);
-        const int ncol = wn * WNT + ni * 16 + 4 * (s & 3);
-        const int c = ncol >> 3;
-        const int b0 = krow * (BN * 2) + ((c ^ (2 * swz_b(krow))) << 4) + ((ncol & 7) << 1);
-        const int b1 = (krow + 4) * (BN * 2) + ((c ^ (2 * swz_b(krow + 4))) << 4) + ((ncol & 7) << 1);
-        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b0));
-        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b1));
-        const short __attribute__((ext_vector_type(8))) both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        bfr[ni] = __builtin_bit_cast(bf16x8, both);
-      }
+      for (int ni = 0; ni < NI; ++ni) bfr[ni] = rd_b(st, ks, ni);
       // swapped operands: D[n][m] = sum_k W[k][n] A[m][k], so each lane ends with
       // 4 consecutive output columns of one row
 #pragma unroll
@@ -274,17 +286,87 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void grouped_gemm_bf16_kernel(cons
     }
   };
 
+  if constexpr (PF) {
+    // Software pipeline over 32-wide k units: the operands of unit u + 1 are read
+    // from LDS into the second register set while the MFMAs of unit u run. A
+    // barrier precedes the first read of each k-tile; before it every wave has
+    // finished its reads of the previous k-tile, whose stage is then refilled.
+    constexpr int KS = BK / 32;
+    constexpr int Q = MI * NI;   // MFMAs per unit
+    constexpr int NR = NI + MI;  // operand reads per unit (a B operand = two transposing reads)
+    bf16x8 fa[2][MI], fb[2][NI];
+    // MFMAs of the unit in set CUR, with the reads of unit (nst, nks) into the other set
+    // spread evenly over them (B operands first: every MFMA of a row tile needs all of them).
+    auto unit = [&](auto cur_c, int nst, int nks) {
+      constexpr int CUR = decltype(cur_c)::value, NXT = CUR ^ 1;
 #pragma unroll
-  for (int t = 0; t < NSTAGE - 1; ++t)
-    if (t < nk) issue(t);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (A_TAIL_W == 0 || wave < A_TAIL_W)
-      wait_tiles<LD_HI, NSTAGE - 2>(min(NSTAGE - 2, nk - 1 - kt));
-    else
-      wait_tiles<LD_LO, NSTAGE - 2>(min(NSTAGE - 2, nk - 1 - kt));
-    block_barrier();  // tile kt is in LDS for every wave; buffer of tile kt-1 is free
-    if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1);
-    compute(kt % NSTAGE);
+      for (int q = 0; q < Q; ++q) {
+        const int mi = q / NI, ni = q % NI;
+        if (!SKIP || mi < mact)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[CUR][ni], fa[CUR][mi], acc[mi][ni], 0, 0, 0);
+        if constexpr (!SKIP) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // this MFMA, then its reads
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          if ((r * Q) / NR != q) continue;
+          if (r < NI) {
+            fb[NXT][r] = rd_b(nst, nks, r);
+            if constexpr (!SKIP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          } else if (!SKIP || r - NI < mact) {
+            fa[NXT][r - NI] = rd_a(nst, nks, r - NI);
+            if constexpr (!SKIP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+      }
+    };
+    auto wait_tile = [&](auto maxrem_c, int rem) {
+      constexpr int MR = decltype(maxrem_c)::value;
+      if (A_TAIL_W == 0 || wave < A_TAIL_W) wait_tiles<LD_HI, MR>(rem);
+      else wait_tiles<LD_LO, MR>(rem);
+    };
+#pragma unroll
+    for (int t = 0; t < NSTAGE; ++t)
+      if (t < nk) issue(t);
+    wait_tile(std::integral_constant<int, NSTAGE - 1>{}, min(NSTAGE - 1, nk - 1));
+    block_barrier();
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) fb[0][ni] = rd_b(0, 0, ni);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+      if (!SKIP || mi < mact) fa[0][mi] = rd_a(0, 0, mi);
+    const int nu = nk * KS;
+    // one unit: u = kt * KS + ks, register set u & 1
+    auto step = [&](auto cur_c, int u) {
+      const int kt = u / KS, ks = u - kt * KS;
+      int nst = kt % NSTAGE, nks = ks + 1;
+      if (nks == KS) {
+        nks = 0;
+        if (kt + 1 < nk) {
+          wait_lgkm0();
+          wait_tile(std::integral_constant<int, NSTAGE - 2>{}, min(NSTAGE - 2, nk - 2 - kt));
+          block_barrier();  // tile kt + 1 is in LDS; every wave is done with tile kt
+          if (kt + NSTAGE < nk) issue(kt + NSTAGE);
+          nst = (kt + 1) % NSTAGE;
+        }
+      }
+      unit(cur_c, nst, nks);
+    };
+    for (int u = 0; u < nu; u += 2) {
+      step(std::integral_constant<int, 0>{}, u);
+      if (u + 1 < nu) step(std::integral_constant<int, 1>{}, u + 1);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < NSTAGE - 1; ++t)
+      if (t < nk) issue(t);
+    for (int kt = 0; kt < nk; ++kt) {
+      if (A_TAIL_W == 0 || wave < A_TAIL_W)
+        wait_tiles<LD_HI, NSTAGE - 2>(min(NSTAGE - 2, nk - 1 - kt));
+      else
+        wait_tiles<LD_LO, NSTAGE - 2>(min(NSTAGE - 2, nk - 1 - kt));
+      block_barrier();  // tile kt is in LDS for every wave; buffer of tile kt-1 is free
+      if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1);
+      compute(kt % NSTAGE);
+    }
   }
 
   // epilogue: lane holds C[m = .. + s][n = .. + 4g + j], j = 0..3, per MFMA tile
@@ -367,7 +449,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 // Grid rounded up to a multiple of the XCD count (surplus workgroups exit at once).
 dim3 grid_for(int64_t tiles) { return dim3((unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds)); }
 
-template <int BM, int BK, int NSTAGE, int ACT, bool SKIP, int NW = 8, int WNT = 64, int BN = 256>
+// PF: the software-pipelined main loop (operands of the next 32-wide k unit read
+// during the MFMAs of the current one), for the compute-bound tile shapes.
+template <int BM, int BK, int NSTAGE, int ACT, bool SKIP, bool PF, int NW = 8, int WNT = 64, int BN = 256>
 hipError_t launch_bf16(const FfnLaunch& a, hipStream_t s) {
   hipError_t err = hipSuccess;
   if (!a.tile_map_ready) {
@@ -376,11 +460,11 @@ hipError_t launch_bf16(const FfnLaunch& a, hipStream_t s) {
   }
   const int64_t mtiles = (a.max_rows + BM - 1) / BM + a.E;
   const int nt1 = (a.f + BN - 1) / BN, nt2 = (a.d + BN - 1) / BN;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, true, SKIP, NW, WNT>), grid_for(mtiles * nt1),
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, true, SKIP, NW, WNT, PF>), grid_for(mtiles * nt1),
                      dim3(64 * NW), 0, s, static_cast<const uint16_t*>(a.x_perm), static_cast<const uint16_t*>(a.w1),
                      static_cast<uint16_t*>(a.h1), a.offsets, a.tile_start, a.E, a.d, a.f, nt1);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, false, SKIP, NW, WNT>), grid_for(mtiles * nt2),
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, false, SKIP, NW, WNT, PF>), grid_for(mtiles * nt2),
                      dim3(64 * NW), 0, s, static_cast<const uint16_t*>(a.h1), static_cast<const uint16_t*>(a.w2),
                      static_cast<uint16_t*>(a.y_perm), a.offsets, a.tile_start, a.E, a.f, a.d, nt2);
   return hipGetLastError();
@@ -425,10 +509,10 @@ template <int ACT>
 hipError_t launch_ffn_act(const FfnLaunch& a, hipStream_t s) {
   switch (ffn_tiles(a.dtype, a.capacity, a.max_rows, a.E)) {
     case kTilesF32: return launch_f32<ACT>(a, s);
-    case kTiles160Skip: return launch_bf16<160, 64, 3, ACT, true>(a, s);
-    case kTiles256Skip: return launch_bf16<256, 32, 4, ACT, true>(a, s);
-    case kTiles256: return launch_bf16<256, 32, 4, ACT, false>(a, s);
-    default: return launch_bf16<128, 64, 3, ACT, false>(a, s);
+    case kTiles160Skip: return launch_bf16<160, 64, 3, ACT, true, false>(a, s);
+    case kTiles256Skip: return launch_bf16<256, 32, 4, ACT, true, true>(a, s);
+    case kTiles256: return launch_bf16<256, 32, 4, ACT, false, true>(a, s);
+    default: return launch_bf16<128, 64, 3, ACT, false, false>(a, s);
   }
 }
 

@@ -40,6 +40,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
+// s_waitcnt lgkmcnt(0): this thread's LDS reads have returned.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Wait until at most rem * LD of this thread's loads are in flight (rem = tiles
 // issued after the one about to be read, LD = loads per thread per tile).
 template <int LD, int MAXREM>

@@ -259,6 +259,10 @@ SMALL = [
     ("gshard_top2", dict(T=1111, E=7, d_model=256, d_ff=1000)),
     ("gshard_top2", dict(T=2048, capacity=17)),
     ("dropless_top1", dict(T=999, d_model=512, d_ff=640)),
+    # 256-row expert tiles: ragged K and N, more tiles than CUs (several per persistent block)
+    ("dropless_top1", dict(T=40000, E=4, d_model=200, d_ff=328)),
+    # 256-row tiles with a capacity between 160 and 256 (row tiles past the segment skipped)
+    ("gshard_top2", dict(T=4000, E=16, capacity=200, d_model=296, d_ff=520)),
 ]
 
 
