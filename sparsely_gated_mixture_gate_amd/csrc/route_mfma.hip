@@ -161,6 +161,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   constexpr int OFF_RES = kTok * HS * 4;
   constexpr int OFF_CV = OFF_RES + kTok * RS * 4;
   constexpr int OFF_CI = OFF_CV + 8 * KK * 64 * 4;
+  static_assert(OFF_CV % 16 == 0, "fallback ring must start on a 16-byte boundary");
   constexpr int OFF_WM = OFF_CI + 8 * KK * 64 * 4;
   constexpr int OFF_WS = OFF_WM + 8 * 64 * 4;
   constexpr int OFF_PART = OFF_WS + 8 * 64 * 4;
@@ -645,15 +646,24 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
         block_barrier();  // stage kt in LDS for every wave; the buffer of stage kt-1 is free
         if (kt + F_STAGES - 1 < fnk) fissue(kt + F_STAGES - 1);
         const char* sb = smem + OFF_CV + (kt % F_STAGES) * F_CH * 16;
-        const uint16_t* sw = reinterpret_cast<const uint16_t*>(sb);
+        lds_char* sw = (lds_char*)(&smem_u4[OFF_CV / 16 + (kt % F_STAGES) * F_CH]);
         const uint4* sx = reinterpret_cast<const uint4*>(sb + F_WCH * 16);
         const int nj = min(F_BK, d - kt * F_BK);  // a multiple of 8
         auto do_q8 = [&](int q8) {
+          // column c's weights of rows 8 q8 .. +7 by two transposing reads: the lanes
+          // of a 16-lane group hold 16 consecutive columns, source lane s points at
+          // row 8 q8 + s/4, columns 4 (s%4) .. +3 of the group
+          const int kr = q8 * 8 + ((lane & 15) >> 2);
+          const int nc = (c - lane) + 16 * (lane >> 4) + 4 * (lane & 3);
+          const int b0 = kr * (NCOL * 2) + (((nc >> 3) ^ swz_w<BCR>(kr)) << 4) + ((nc & 7) << 1);
+          const int b1 = (kr + 4) * (NCOL * 2) + (((nc >> 3) ^ swz_w<BCR>(kr + 4)) << 4) + ((nc & 7) << 1);
+          const shortx4 wlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sw + b0));
+          const shortx4 whi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sw + b1));
           float wv[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int jj = q8 * 8 + u;
-            wv[u] = bf16_to_f32(sw[jj * NCOL + (((c >> 3) ^ swz_w<BCR>(jj)) << 3) + (c & 7)]);
+          for (int u = 0; u < 4; ++u) {
+            wv[u] = bf16_to_f32((uint16_t)wlo[u]);
+            wv[u + 4] = bf16_to_f32((uint16_t)whi[u]);
           }
           uint4 xv[NF];
 #pragma unroll
