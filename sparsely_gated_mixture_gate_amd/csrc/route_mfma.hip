@@ -637,6 +637,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
       float accv[NF];
 #pragma unroll
       for (int q = 0; q < NF; ++q) accv[q] = 0.0f;
+      const bool busy = base + f0 * NF < nflag;  // wave-uniform (a wave's columns share one token slot)
       const int fnk = (d + F_BK - 1) / F_BK;
 #pragma unroll
       for (int t = 0; t < F_STAGES - 1; ++t)
@@ -677,7 +678,9 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
               accv[q] = __builtin_fmaf(xs, wv[u], accv[q]);
             }
         };
-        if (nj == F_BK) {
+        if (!busy) {
+          // token slot past the flagged tokens: loads and barriers only
+        } else if (nj == F_BK) {
 #pragma unroll
           for (int q8 = 0; q8 < F_CPR; ++q8) do_q8(q8);  // full stage: every LDS read can be issued early
         } else {
