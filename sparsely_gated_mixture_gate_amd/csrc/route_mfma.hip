@@ -168,20 +168,26 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   constexpr int POST = OFF_PART + 4 * 512 * 4;
   constexpr int SMEM0 = RING > POST ? RING : POST;
   // fallback ring, from OFF_CV on: per stage the weight tile [F_BK][NCOL] and
-  // the x rows of 16 flagged tokens [16][F_BK]; F_BK = 32, or 16 / 8 where the
-  // weight tile is wide, so that at least 4 stages fit the free LDS
-  constexpr int FR = 16;                         // tokens per fallback round
-  constexpr int F_FREE = SMEM0 - OFF_CV;
-  constexpr int F_BK = F_FREE / ((32 * BCR + FR * 4) * 16) >= 4 ? 32
-                     : (F_FREE / ((16 * BCR + FR * 2) * 16) >= 4 ? 16 : 8);
+  // the x rows of 16 flagged tokens [16][F_BK]; F_BK = 64, 32, 16 or 8 rows, the
+  // largest of which 3 stages fit (fewer stages, fewer barriers along the chains).
+  // A block that holds more than half the LDS runs alone on its CU anyway, so its
+  // fallback ring may grow to 152 KB.
+  constexpr int FR = 16;  // tokens per fallback round
+  constexpr int F_FREE = (SMEM0 > 80 * 1024 ? 152 * 1024 : SMEM0) - OFF_CV;
+  constexpr int F_BK = F_FREE / ((64 * BCR + FR * 8) * 16) >= 3   ? 64
+                       : F_FREE / ((32 * BCR + FR * 4) * 16) >= 3 ? 32
+                       : F_FREE / ((16 * BCR + FR * 2) * 16) >= 3 ? 16
+                                                                  : 8;
   constexpr int F_CPR = F_BK / 8;                // x chunks per row per stage
   constexpr int F_WCH = F_BK * BCR;              // weight chunks per stage
   constexpr int F_XCH = FR * F_CPR;              // x chunks per stage
   constexpr int F_CH = F_WCH + F_XCH;            // chunks per fallback stage
   constexpr int F_NR = (F_CH + 511) / 512;
   constexpr int F_STAGES = F_FREE / (F_CH * 16) < 8 ? F_FREE / (F_CH * 16) : 8;
-  constexpr int SMEM = SMEM0;
-  static_assert(F_WCH % 64 == 0 && F_STAGES >= 3 && SMEM + 1024 <= 160 * 1024, "LDS");
+  constexpr int SMEM = SMEM0 > OFF_CV + F_STAGES * F_CH * 16 ? SMEM0 : OFF_CV + F_STAGES * F_CH * 16;
+  static_assert(F_WCH % 64 == 0 && F_STAGES >= 3 && F_NR <= 5 && NR <= 5 &&
+                    SMEM + 1024 <= 160 * 1024,
+                "LDS");
   __shared__ uint4 smem_u4[SMEM / 16];
   __shared__ float bmax_s[kTok];
   __shared__ int flist_s[kTok];
@@ -629,7 +635,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
           const uint32_t dst = fl0 + (uint32_t)((st * F_CH + i * 512 + wave * 64) * 16);
           if (fisW[i]) {
             load_to_lds(__builtin_amdgcn_readfirstlane(dst), (int)(fvoff[i] + (uint32_t)(kt * F_BK * NCOL * 2)), rsW, 0);
-          } else if (tid + 512 * i < F_WCH + RT * F_CPR) {  // x chunks of this round's rows
+          } else if (tid + 512 * i < F_CH) {  // x chunks: every slot loads (slots past this round's rows repeat a
+                                               // valid row), so every wave with fact[i] issues the load its waits count
             load_to_lds(__builtin_amdgcn_readfirstlane(dst), (int)(fvoff[i] + (uint32_t)(kt * F_BK * 2)), rsXall, 0);
           }
         }
