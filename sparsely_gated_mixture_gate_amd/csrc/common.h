@@ -111,6 +111,8 @@ struct DispatchLaunch {
   int32_t* blk_cnt;  // [E][nb] workspace
   int32_t* tile_start;  // [E+1] M-tile prefix for the expert FFN, or null
   int tile_rows;        // M-tile rows of that prefix
+  bool skip_permute;    // x_perm is not written (the expert FFN gathers its rows from x)
+  void* y_zero;         // top-1 layers only: y [T, d], whose rows of dropped tokens are zeroed (or null)
 };
 int64_t dispatch_num_blocks(int64_t assignments);
 hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s);
@@ -127,6 +129,14 @@ struct FfnLaunch {
   void* h1;             // [max_rows, f] dtype workspace
   int32_t* tile_start;  // [E+1] workspace
   bool tile_map_ready;  // tile_start already holds the M-tile prefix (built by the dispatch scan)
+  // bf16 forward path (optional): layer 1 gathers row r from x_src[row_src[r]] instead of
+  // x_perm[r]; with y_out set (top-1 layers), layer 2 writes gate[t] * row into
+  // y_out[t], t = row_src[r], instead of y_perm[r]
+  const void* x_src;
+  const int32_t* row_src;
+  int64_t T;
+  void* y_out;
+  const float* gate;
 };
 hipError_t launch_expert_ffn(const FfnLaunch& a, hipStream_t s);
 int ffn_tile_rows(int dtype, int64_t capacity, int64_t max_rows, int E);  // M-tile rows the FFN launch uses

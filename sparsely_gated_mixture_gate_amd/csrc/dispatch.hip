@@ -87,7 +87,8 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
                                                             const int32_t* __restrict__ blk_base,
                                                             const int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ slot_dest,
-                                                            int32_t* __restrict__ row_src) {
+                                                            int32_t* __restrict__ row_src,
+                                                            uint4* __restrict__ y_zero, int y_chunks) {
   extern __shared__ int wcnt[];  // [4 waves][E] running counts
   for (int i = threadIdx.x; i < 4 * E; i += 256) wcnt[i] = 0;
   __syncthreads();
@@ -116,9 +117,11 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
+  bool dropped[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = ex[q];
+    dropped[q] = false;
     if (e < 0) continue;
     const int64_t a = base + q * 64 + lane;
     int64_t r = (int64_t)blk_base[(int64_t)e * nb + blockIdx.x] + loc[q];
@@ -127,6 +130,21 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
     const int32_t slot = keep ? (int32_t)(offsets[e] + r) : -1;
     slot_dest[a] = slot;
     if (keep) row_src[slot] = (int32_t)(a / k);
+    dropped[q] = !keep;
+  }
+  // top-1 layers: the output rows of dropped tokens are zero; the wave clears them
+  // together, one row at a time, with coalesced 16-byte stores
+  if (y_zero) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint64_t m = __ballot(dropped[q]);
+      while (m) {
+        const int j = __builtin_ctzll(m);
+        m &= m - 1;
+        uint4* yr = y_zero + (base + q * 64 + j) * y_chunks;  // k = 1: assignment = token
+        for (int c = lane; c < y_chunks; c += 64) yr[c] = uint4{0u, 0u, 0u, 0u};
+      }
+    }
   }
 }
 
@@ -166,12 +184,13 @@ hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s) {
   int nbits = 0;
   while ((1 << nbits) < a.E) ++nbits;
   hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nb), dim3(256), sizeof(int) * 4 * a.E, s, a.topk_idx, n, a.k, a.E,
-                     nbits, nb, a.C, a.blk_cnt, a.offsets, a.slot_dest, a.row_src);
+                     nbits, nb, a.C, a.blk_cnt, a.offsets, a.slot_dest, a.row_src, static_cast<uint4*>(a.y_zero),
+                     a.d * (a.dtype == 1 ? 2 : 4) / 16);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int elt = a.dtype == 1 ? 2 : 4;
   const int cpr = a.d * elt / 16;
   const int64_t total = a.max_rows * cpr;
-  if (total > 0) {
+  if (total > 0 && !a.skip_permute) {
     hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        static_cast<const uint4*>(a.x), a.row_src, a.offsets, a.E, cpr, total,
                        static_cast<uint4*>(a.x_perm));

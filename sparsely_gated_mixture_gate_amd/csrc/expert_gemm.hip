@@ -148,7 +148,12 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
                                                                 uint16_t* __restrict__ C,
                                                                 const int32_t* __restrict__ offsets,
                                                                 const int32_t* __restrict__ tile_start, int E,
-                                                                int K, int N, int n_tiles_n) {
+                                                                int K, int N, int n_tiles_n,
+                                                                const int32_t* __restrict__ a_map, int64_t a_rows,
+                                                                const int32_t* __restrict__ c_map,
+                                                                const float* __restrict__ c_scale) {
+  // a_map (or null): A row r of a segment is row a_map[r] of the a_rows-row buffer A.
+  // c_map (or null): C row r is written to row c_map[r], scaled by c_scale[c_map[r]].
   constexpr int NT = 64 * NW;            // threads
   constexpr int WN_W = BN / WNT;         // waves along N
   constexpr int WM_W = NW / WN_W;        // waves along M
@@ -187,7 +192,28 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
   // segment are clamped (read, never stored). In the last, partial k-tile the A
   // chunks past K are clamped inside the row (finite data) and the B rows past K
   // (and B columns past N throughout) point outside the buffer, which loads zero.
-  const int32x4 rsA = buffer_rsrc(A + (int64_t)row0 * K, (uint32_t)rows * K * 2);
+  // scattered output rows: their targets and scales are loaded now, so the loads
+  // complete under the main loop
+  int64_t orow_m[MI];
+  float scale_m[MI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    orow_m[mi] = 0;
+    scale_m[mi] = 1.0f;
+  }
+  if (c_map) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int grow = row0 + (wave / WN_W) * WM + mi * 16 + (tid & 15);
+      if (grow < row_end) {
+        orow_m[mi] = c_map[grow];
+        scale_m[mi] = c_scale[orow_m[mi]];
+      }
+    }
+  }
+  const bool gather = a_map != nullptr;
+  const int32x4 rsA = gather ? buffer_rsrc(A, (uint32_t)(a_rows * K * 2))
+                             : buffer_rsrc(A + (int64_t)row0 * K, (uint32_t)rows * K * 2);
   const int32x4 rsB = buffer_rsrc(W + (int64_t)e * K * N, (uint32_t)K * N * 2);
   constexpr int kOut = 0x7FFFFFF0;  // byte offset past any operand (K*N*2 < 2^31 - 16 is checked on the host)
   int voffA[A_LD], voffA_last[A_LD], voffB[B_LD], voffB_last[B_LD];
@@ -197,9 +223,12 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
     const int row = c / RC, phys = c % RC;
     const int kc = phys ^ swz_a_rc<RC>(row);
     const int lrow = min(row, rows - 1);
-    voffA[i] = (lrow * K + kc * 8) * 2;
-    voffA_last[i] = (lrow * K + min(kc * 8, K - k_last - 8)) * 2;  // + soffset k_last*2
-    if (SKIP && row >= rows) voffA[i] = voffA_last[i] = kOut;  // rows past the segment load zero
+    // row of the A buffer (gathered rows: T * K * 2 < 2^32 is checked on the host)
+    const uint32_t arow = gather ? (uint32_t)a_map[row0 + lrow] : (uint32_t)lrow;
+    voffA[i] = (int)((arow * (uint32_t)K + (uint32_t)(kc * 8)) * 2u);
+    voffA_last[i] = (int)((arow * (uint32_t)K + (uint32_t)min(kc * 8, K - k_last - 8)) * 2u);  // + soffset k_last*2
+    // rows past the segment load zero (gathered: they repeat the last row; never stored either way)
+    if (SKIP && row >= rows && !gather) voffA[i] = voffA_last[i] = kOut;
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
@@ -374,17 +403,22 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
   for (int mi = 0; mi < MI; ++mi) {
     const int grow = row0 + wm * WM + mi * 16 + s;
     if (grow >= row_end) continue;
+    const int64_t orow = c_map ? orow_m[mi] : grow;
+    const float scale = scale_m[mi];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int gcol = n0 + wn * WNT + ni * 16 + 4 * g;
       if (gcol >= N) continue;
       float v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = APPLY_ACT ? activation_bf16<ACT>(acc[mi][ni][j]) : acc[mi][ni][j];
+      for (int j = 0; j < 4; ++j) {
+        v[j] = APPLY_ACT ? activation_bf16<ACT>(acc[mi][ni][j]) : acc[mi][ni][j];
+        if (c_map) v[j] = scale * v[j];
+      }
       uint2 o;
       o.x = pack_bf16x2(v[0], v[1]);
       o.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(C + (int64_t)grow * N + gcol) = o;
+      *reinterpret_cast<uint2*>(C + orow * N + gcol) = o;
     }
   }
 }
@@ -461,12 +495,14 @@ hipError_t launch_bf16(const FfnLaunch& a, hipStream_t s) {
   const int64_t mtiles = (a.max_rows + BM - 1) / BM + a.E;
   const int nt1 = (a.f + BN - 1) / BN, nt2 = (a.d + BN - 1) / BN;
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, true, SKIP, NW, WNT, PF>), grid_for(mtiles * nt1),
-                     dim3(64 * NW), 0, s, static_cast<const uint16_t*>(a.x_perm), static_cast<const uint16_t*>(a.w1),
-                     static_cast<uint16_t*>(a.h1), a.offsets, a.tile_start, a.E, a.d, a.f, nt1);
+                     dim3(64 * NW), 0, s, static_cast<const uint16_t*>(a.x_src ? a.x_src : a.x_perm),
+                     static_cast<const uint16_t*>(a.w1), static_cast<uint16_t*>(a.h1), a.offsets, a.tile_start, a.E,
+                     a.d, a.f, nt1, a.x_src ? a.row_src : nullptr, a.T, nullptr, nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, false, SKIP, NW, WNT, PF>), grid_for(mtiles * nt2),
                      dim3(64 * NW), 0, s, static_cast<const uint16_t*>(a.h1), static_cast<const uint16_t*>(a.w2),
-                     static_cast<uint16_t*>(a.y_perm), a.offsets, a.tile_start, a.E, a.f, a.d, nt2);
+                     static_cast<uint16_t*>(a.y_out ? a.y_out : a.y_perm), a.offsets, a.tile_start, a.E, a.f, a.d, nt2,
+                     nullptr, 0, a.y_out ? a.row_src : nullptr, a.y_out ? a.gate : nullptr);
   return hipGetLastError();
 }
 

@@ -235,7 +235,7 @@ moe_status run_route(const moe_params* p, const void* x, const void* w_gate, con
 
 moe_status run_dispatch(const moe_params* p, const void* x, const int32_t* topk_idx, int32_t* counts_kept,
                         int32_t* offsets, int32_t* slot_dest, int32_t* row_src, void* x_perm, int32_t* blk_cnt,
-                        int32_t* tile_start, hipStream_t s) {
+                        int32_t* tile_start, bool skip_permute, void* y_zero, hipStream_t s) {
   DispatchLaunch a;
   a.T = p->T;
   a.d = p->d_model;
@@ -254,12 +254,17 @@ moe_status run_dispatch(const moe_params* p, const void* x, const int32_t* topk_
   a.blk_cnt = blk_cnt;
   a.tile_start = tile_start;
   a.tile_rows = tile_start ? ffn_tile_rows(p->dtype, capacity_of(p), max_rows_of(p), p->E) : 0;
+  a.skip_permute = skip_permute;
+  a.y_zero = y_zero;
   const hipError_t e = launch_dispatch(a, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "dispatch launch");
 }
 
+// x_src / row_src (or null): layer 1 gathers its rows from x; y_out / gate (or null,
+// top-1 bf16 layers only): layer 2 writes the gated rows straight into y.
 moe_status run_ffn(const moe_params* p, const void* x_perm, const int32_t* offsets, const void* w1, const void* w2,
-                   void* y_perm, const FfnWs& w, bool tile_map_ready, hipStream_t s) {
+                   void* y_perm, const FfnWs& w, bool tile_map_ready, hipStream_t s, const void* x_src = nullptr,
+                   const int32_t* row_src = nullptr, void* y_out = nullptr, const float* gate = nullptr) {
   FfnLaunch a;
   a.d = p->d_model;
   a.f = p->d_ff;
@@ -276,6 +281,11 @@ moe_status run_ffn(const moe_params* p, const void* x_perm, const int32_t* offse
   a.h1 = w.h1;
   a.tile_start = w.tile_start;
   a.tile_map_ready = tile_map_ready;
+  a.x_src = x_src;
+  a.row_src = row_src;
+  a.T = p->T;
+  a.y_out = y_out;
+  a.gate = gate;
   const hipError_t e = launch_expert_ffn(a, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "expert FFN launch");
 }
@@ -369,7 +379,7 @@ moe_status moe_dispatch(const moe_params* p, const void* x, const int32_t* topk_
   if ((st = check_ws(p, MOE_OP_DISPATCH, false, ws, ws_bytes)) != MOE_OK) return st;
   Carver c(ws);
   int32_t* blk = carve_dispatch(c, p);
-  return run_dispatch(p, x, topk_idx, counts_kept, offsets, slot_dest, row_src, x_perm, blk, nullptr,
+  return run_dispatch(p, x, topk_idx, counts_kept, offsets, slot_dest, row_src, x_perm, blk, nullptr, false, nullptr,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -429,10 +439,18 @@ moe_status moe_forward(const moe_params* p, const void* x, const void* w_gate, c
   if ((st = run_route(p, x, w_gate, gate_bias, w_noise, noise, idx, gate, cr, aux_out, nullptr, w.route, s)) !=
       MOE_OK)
     return st;
-  if ((st = run_dispatch(p, x, idx, ck, w.offsets, sd, w.row_src, w.x_perm, w.blk_cnt, w.ffn.tile_start, s)) !=
-      MOE_OK)
+  // bf16: the expert GEMM gathers its rows from x (no x_perm copy); top-1 layers also
+  // write the gated expert outputs straight into y (no combine pass; the dispatch
+  // zeroes the rows of dropped tokens)
+  const bool fused = p->dtype == MOE_BF16;
+  const bool direct_y = fused && p->k == 1;
+  if ((st = run_dispatch(p, x, idx, ck, w.offsets, sd, w.row_src, w.x_perm, w.blk_cnt, w.ffn.tile_start, fused,
+                         direct_y ? y : nullptr, s)) != MOE_OK)
     return st;
-  if ((st = run_ffn(p, w.x_perm, w.offsets, w1, w2, w.y_perm, w.ffn, true, s)) != MOE_OK) return st;
+  if ((st = run_ffn(p, w.x_perm, w.offsets, w1, w2, w.y_perm, w.ffn, true, s, fused ? x : nullptr,
+                    fused ? w.row_src : nullptr, direct_y ? y : nullptr, direct_y ? gate : nullptr)) != MOE_OK)
+    return st;
+  if (direct_y) return MOE_OK;
   return run_combine(p, w.y_perm, sd, gate, y, s);
 }
 
