@@ -189,7 +189,11 @@ moe_status moe_combine(const moe_params* p, const void* y_perm, const int32_t* s
 
 /*
  * moe_forward -- the whole layer: moe_route, moe_dispatch, moe_expert_ffn and
- * moe_combine on one stream, intermediates in `ws`.
+ * moe_combine on one stream, intermediates in `ws`. For bf16 layers the expert
+ * GEMM reads its rows straight from x (x_perm is not materialised); for top-1
+ * bf16 layers it also writes y[t] = topk_gate[t] * (expert output) directly, in
+ * fp32 rounded once to bf16 (moe_combine would round the expert output to bf16
+ * first), and the rows of dropped tokens are zeroed by the dispatch.
  * Inputs as moe_route plus w1, w2. Outputs: y [T,d] dtype (required);
  * aux_out [3], topk_idx [T,k], topk_gate [T,k], counts_routed [E], counts_kept [E],
  * slot_dest [T,k] -- each optional (NULL: kept in the workspace only).
