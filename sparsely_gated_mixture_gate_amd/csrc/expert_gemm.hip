@@ -13,13 +13,16 @@
 //     ceil(rows_e / BM) M-tiles per expert; GEMM blocks binary-search it, so the
 //     host never synchronises on the ragged segment sizes. The grid is an upper
 //     bound (ceil(R_max / BM) + E M-tiles); surplus blocks exit at once.
-//   * bf16 path: BM x 256 x BK tiles, 512 threads = 2 x 4 waves of
-//     (BM/2) x 64, MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation. Tile
-//     shape by the rows an expert can hold: capacity <= 160 -> 160 x 256 x 64
-//     (3 stages), capacity <= 256 -> 256 x 256 x 32 (4 stages), both one M-tile
-//     per expert with 16-row MFMA tiles past the segment skipped and their A rows
-//     loaded as zero; otherwise about one tile of rows per expert -> 128 x 256 x 64
-//     (3 stages), large segments -> 256 x 256 x 32 (4 stages). Both operands go
+//   * bf16 path: BM x BN x BK tiles, 512 threads = 2 x 4 waves of
+//     (BM/2) x (BN/4), MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation. Tile
+//     shape by the rows an expert can hold: capacity <= 160 -> 160 x 512 x 32
+//     (layer 1, 3 stages) and 160 x 384 x 32 (layer 2, 4 stages), capacity <= 256
+//     -> 256 x 256 x 32 (4 stages), both one M-tile per expert with 16-row MFMA
+//     tiles past the segment skipped and their A rows loaded as zero; otherwise
+//     about one tile of rows per expert -> 128 x 512 x 32 (3 stages), large
+//     segments -> 256 x 256 x 32 (4 stages). Where weights stream from HBM, wide
+//     N-tiles re-read each expert's rows fewer times and read fewer LDS operand
+//     bytes per weight byte (those reads compete with the weight loads). Both operands go
 //     HBM -> LDS in their HBM layout by direct-to-LDS buffer loads (16-byte
 //     chunks, XOR-swizzled per row against bank conflicts) into an NSTAGE-deep
 //     ring, NSTAGE - 1 k-tiles in flight, explicit vmcnt waits and a fence-free
@@ -42,6 +45,7 @@
 
 #include "common.h"
 #include "lds_dma.h"
+
 
 
 namespace moe {
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
   constexpr int STAGE_CH = A_CH + B_CH;
   static_assert(A_CH % 64 == 0 && B_CH % NT == 0 && WN_W * WM_W == NW, "tile / thread mismatch");
   static_assert(NSTAGE >= 2 && NSTAGE <= 5, "stages");
-  static_assert((BN == 128 || BN == 256) && WM % 16 == 0, "tile shape");
+  static_assert((BN == 128 || BN == 256 || BN == 384 || BN == 512) && WM % 16 == 0 && WNT % 16 == 0, "tile shape");
   __shared__ uint4 smem[NSTAGE * STAGE_CH];
 
   int e, row0, row_end, nt;
@@ -485,7 +489,9 @@ dim3 grid_for(int64_t tiles) { return dim3((unsigned)(((tiles + kXcds - 1) / kXc
 
 // PF: the software-pipelined main loop (operands of the next 32-wide k unit read
 // during the MFMAs of the current one), for the compute-bound tile shapes.
-template <int BM, int BK, int NSTAGE, int ACT, bool SKIP, bool PF, int NW = 8, int WNT = 64, int BN = 256>
+// BK, NSTAGE, BN, WNT: layer 2 (and layer 1 unless BK1 .. WNT1 are given).
+template <int BM, int BK, int NSTAGE, int ACT, bool SKIP, bool PF, int NW = 8, int WNT = 64, int BN = 256,
+          int BK1 = BK, int NSTAGE1 = NSTAGE, int BN1 = BN, int WNT1 = WNT>
 hipError_t launch_bf16(const FfnLaunch& a, hipStream_t s) {
   hipError_t err = hipSuccess;
   if (!a.tile_map_ready) {
@@ -493,8 +499,8 @@ hipError_t launch_bf16(const FfnLaunch& a, hipStream_t s) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int64_t mtiles = (a.max_rows + BM - 1) / BM + a.E;
-  const int nt1 = (a.f + BN - 1) / BN, nt2 = (a.d + BN - 1) / BN;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, true, SKIP, NW, WNT, PF>), grid_for(mtiles * nt1),
+  const int nt1 = (a.f + BN1 - 1) / BN1, nt2 = (a.d + BN - 1) / BN;
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN1, BK1, NSTAGE1, ACT, true, SKIP, NW, WNT1, PF>), grid_for(mtiles * nt1),
                      dim3(64 * NW), 0, s, static_cast<const uint16_t*>(a.x_src ? a.x_src : a.x_perm),
                      static_cast<const uint16_t*>(a.w1), static_cast<uint16_t*>(a.h1), a.offsets, a.tile_start, a.E,
                      a.d, a.f, nt1, a.x_src ? a.row_src : nullptr, a.T, nullptr, nullptr);
@@ -545,10 +551,13 @@ template <int ACT>
 hipError_t launch_ffn_act(const FfnLaunch& a, hipStream_t s) {
   switch (ffn_tiles(a.dtype, a.capacity, a.max_rows, a.E)) {
     case kTilesF32: return launch_f32<ACT>(a, s);
-    case kTiles160Skip: return launch_bf16<160, 64, 3, ACT, true, false>(a, s);
+    // weight-streaming, one M-tile per expert: wide N-tiles (fewer re-reads of each
+    // expert's rows, fewer LDS operand reads per weight byte): layer 1 512 columns,
+    // layer 2 384 columns (two tiles of a 768-wide output)
+    case kTiles160Skip: return launch_bf16<160, 32, 4, ACT, true, false, 8, 96, 384, 32, 3, 512, 128>(a, s);
     case kTiles256Skip: return launch_bf16<256, 32, 4, ACT, true, true>(a, s);
     case kTiles256: return launch_bf16<256, 32, 4, ACT, false, true>(a, s);
-    default: return launch_bf16<128, 64, 3, ACT, false, false>(a, s);
+    default: return launch_bf16<128, 32, 3, ACT, false, false, 8, 128, 512, 32, 3, 512, 128>(a, s);
   }
 }
 
