@@ -81,6 +81,7 @@ struct RouteLaunch {
   float* lg;         // route_logit_floats(T, E, noisy): logits H [, clean logits, softplus of noise logits]
   uint16_t* wcat;    // route_wcat_elems(d, E, noisy): bf16 gate (+ noise) weights of the MFMA gate
   int gate_mode;     // MOE_GATE_*
+  bool defer_tail;   // leave the partial sums and the losses to the dispatch (forward path)
   float* part_prob;  // [E][nblk]
   float* part_imp;   // [E][nblk]
   float* part_load;  // [E][nblk]
@@ -113,6 +114,17 @@ struct DispatchLaunch {
   int tile_rows;        // M-tile rows of that prefix
   bool skip_permute;    // x_perm is not written (the expert FFN gathers its rows from x)
   void* y_zero;         // top-1 layers only: y [T, d], whose rows of dropped tokens are zeroed (or null)
+  // forward path (optional, route_tail): the end of the routing step -- fixed-order
+  // sums of the gate's per-block partials (extra blocks of the count kernel) and
+  // the losses (end of the scan kernel)
+  bool route_tail;
+  const float *part_prob, *part_imp, *part_load;
+  const int32_t* part_cnt;
+  int route_nblk;
+  int32_t* counts_routed;
+  double* red;
+  float* aux_out;  // or null
+  int noisy;
 };
 int64_t dispatch_num_blocks(int64_t assignments);
 hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s);

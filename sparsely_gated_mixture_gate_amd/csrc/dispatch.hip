@@ -19,14 +19,25 @@
 //   permute one 16-byte chunk per thread: x_perm[r] = x[row_src[r]], reads of
 //           whole rows, fully coalesced writes.
 #include "common.h"
+#include "route_tail.h"
 
 namespace moe {
 namespace {
 
 constexpr int kChunk = 1024;  // assignments per block: 4 waves x 4 steps x 64 lanes
 
+// Blocks [0, nb): per-block expert histograms. Blocks past nb (forward path): the
+// routing step's per-expert sums, one expert per wave.
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx, int64_t n, int E,
-                                                             int nb, int32_t* __restrict__ blk_cnt) {
+                                                             int nb, int32_t* __restrict__ blk_cnt,
+                                                             const DispatchLaunch tl) {
+  if ((int)blockIdx.x >= nb) {
+    const int e = ((int)blockIdx.x - nb) * 4 + (threadIdx.x >> 6);
+    if (e < E)
+      tail::reduce_expert(e, threadIdx.x & 63, tl.part_prob, tl.part_imp, tl.part_load, tl.part_cnt, tl.route_nblk,
+                          E, tl.counts_routed, tl.red);
+    return;
+  }
   extern __shared__ int hist[];
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
   __syncthreads();
@@ -42,8 +53,12 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ blk_cnt, int nb, int E,
                                                              int64_t C, int32_t* __restrict__ counts_kept,
                                                              int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ tile_start, int tile_rows) {
+                                                             int32_t* __restrict__ tile_start, int tile_rows,
+                                                             const int32_t* __restrict__ counts_routed,
+                                                             const double* __restrict__ red, int64_t T, int k,
+                                                             int noisy, float* __restrict__ aux_out) {
   __shared__ int64_t sc[1024];
+  __shared__ double sh[1024];
   const int e = threadIdx.x;
   int64_t run = 0;
   if (e < E) {
@@ -66,20 +81,23 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
   }
   if (e < E) offsets[e] = (int32_t)(sc[e] - kept);
   if (e == E - 1) offsets[E] = (int32_t)sc[e];
-  if (!tile_start) return;
-  // prefix of ceil(kept / tile_rows) M-tiles per expert for the expert FFN
-  const int64_t tiles = (kept + tile_rows - 1) / tile_rows;
-  __syncthreads();
-  sc[e] = tiles;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int64_t v = e >= off ? sc[e - off] : 0;
+  if (tile_start) {
+    // prefix of ceil(kept / tile_rows) M-tiles per expert for the expert FFN
+    const int64_t tiles = (kept + tile_rows - 1) / tile_rows;
     __syncthreads();
-    sc[e] += v;
+    sc[e] = tiles;
     __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int64_t v = e >= off ? sc[e - off] : 0;
+      __syncthreads();
+      sc[e] += v;
+      __syncthreads();
+    }
+    if (e < E) tile_start[e] = (int32_t)(sc[e] - tiles);
+    if (e == E - 1) tile_start[E] = (int32_t)sc[e];
   }
-  if (e < E) tile_start[e] = (int32_t)(sc[e] - tiles);
-  if (e == E - 1) tile_start[E] = (int32_t)sc[e];
+  // forward path: the balancing losses from the per-expert sums of the count kernel
+  if (aux_out) tail::aux_block<1024>(counts_routed, red, E, T, k, noisy, aux_out, sh);
 }
 
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __restrict__ idx, int64_t n, int k,
@@ -172,13 +190,15 @@ hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s) {
   const int64_t n = a.T * a.k;
   const int nb = (int)dispatch_num_blocks(n);
   hipError_t err;
-  if (nb > 0) {
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nb), dim3(256), sizeof(int) * a.E, s, a.topk_idx, n, a.E, nb,
-                       a.blk_cnt);
+  const int nred = a.route_tail ? (a.E + 3) / 4 : 0;  // blocks of the routing step's per-expert sums
+  if (nb + nred > 0) {
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nb + nred), dim3(256), sizeof(int) * a.E, s, a.topk_idx, n, a.E,
+                       nb, a.blk_cnt, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, a.blk_cnt, nb, a.E, a.C, a.counts_kept,
-                     a.offsets, a.tile_start, a.tile_rows);
+                     a.offsets, a.tile_start, a.tile_rows, a.counts_routed, a.red, a.T, a.k, a.noisy,
+                     a.route_tail ? a.aux_out : nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (nb == 0) return hipSuccess;
   int nbits = 0;

@@ -202,7 +202,8 @@ moe_status check_route_inputs(const moe_params* p, const void* x, const void* w_
 
 moe_status run_route(const moe_params* p, const void* x, const void* w_gate, const float* gate_bias,
                      const void* w_noise, const float* noise, int32_t* topk_idx, float* topk_gate,
-                     int32_t* counts_routed, float* aux_out, float* logits_out, const RouteWs& w, hipStream_t s) {
+                     int32_t* counts_routed, float* aux_out, float* logits_out, const RouteWs& w, hipStream_t s,
+                     bool defer_tail = false) {
   RouteLaunch a;
   a.T = p->T;
   a.d = p->d_model;
@@ -229,13 +230,16 @@ moe_status run_route(const moe_params* p, const void* x, const void* w_gate, con
   a.part_load = w.part_load;
   a.part_cnt = w.part_cnt;
   a.red = w.red;
+  a.defer_tail = defer_tail;
   const hipError_t e = launch_route(a, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "route launch");
 }
 
 moe_status run_dispatch(const moe_params* p, const void* x, const int32_t* topk_idx, int32_t* counts_kept,
                         int32_t* offsets, int32_t* slot_dest, int32_t* row_src, void* x_perm, int32_t* blk_cnt,
-                        int32_t* tile_start, bool skip_permute, void* y_zero, hipStream_t s) {
+                        int32_t* tile_start, bool skip_permute, void* y_zero, hipStream_t s,
+                        const RouteWs* route_tail = nullptr, int32_t* counts_routed = nullptr,
+                        float* aux_out = nullptr, bool noisy = false) {
   DispatchLaunch a;
   a.T = p->T;
   a.d = p->d_model;
@@ -256,6 +260,16 @@ moe_status run_dispatch(const moe_params* p, const void* x, const int32_t* topk_
   a.tile_rows = tile_start ? ffn_tile_rows(p->dtype, capacity_of(p), max_rows_of(p), p->E) : 0;
   a.skip_permute = skip_permute;
   a.y_zero = y_zero;
+  a.route_tail = route_tail != nullptr;
+  a.part_prob = route_tail ? route_tail->part_prob : nullptr;
+  a.part_imp = route_tail ? route_tail->part_imp : nullptr;
+  a.part_load = route_tail ? route_tail->part_load : nullptr;
+  a.part_cnt = route_tail ? route_tail->part_cnt : nullptr;
+  a.route_nblk = p->T > 0 ? (int)((p->T + route_tokens_per_block(p->E, noisy) - 1) / route_tokens_per_block(p->E, noisy)) : 0;
+  a.counts_routed = counts_routed;
+  a.red = route_tail ? route_tail->red : nullptr;
+  a.aux_out = aux_out;
+  a.noisy = noisy ? 1 : 0;
   const hipError_t e = launch_dispatch(a, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "dispatch launch");
 }
@@ -436,7 +450,8 @@ moe_status moe_forward(const moe_params* p, const void* x, const void* w_gate, c
   int32_t* cr = counts_routed ? counts_routed : w.counts_routed;
   int32_t* ck = counts_kept ? counts_kept : w.counts_kept;
   int32_t* sd = slot_dest ? slot_dest : w.slot_dest;
-  if ((st = run_route(p, x, w_gate, gate_bias, w_noise, noise, idx, gate, cr, aux_out, nullptr, w.route, s)) !=
+  // the route's per-expert sums and losses run inside the dispatch kernels
+  if ((st = run_route(p, x, w_gate, gate_bias, w_noise, noise, idx, gate, cr, aux_out, nullptr, w.route, s, true)) !=
       MOE_OK)
     return st;
   // bf16: the expert GEMM gathers its rows from x (no x_perm copy); top-1 layers also
@@ -445,7 +460,7 @@ moe_status moe_forward(const moe_params* p, const void* x, const void* w_gate, c
   const bool fused = p->dtype == MOE_BF16;
   const bool direct_y = fused && p->k == 1;
   if ((st = run_dispatch(p, x, idx, ck, w.offsets, sd, w.row_src, w.x_perm, w.blk_cnt, w.ffn.tile_start, fused,
-                         direct_y ? y : nullptr, s)) != MOE_OK)
+                         direct_y ? y : nullptr, s, &w.route, cr, aux_out, noisy)) != MOE_OK)
     return st;
   if ((st = run_ffn(p, w.x_perm, w.offsets, w1, w2, w.y_perm, w.ffn, true, s, fused ? x : nullptr,
                     fused ? w.row_src : nullptr, direct_y ? y : nullptr, direct_y ? gate : nullptr)) != MOE_OK)

@@ -34,6 +34,7 @@
 #include "common.h"
 #include "lds_dma.h"
 #include "route_common.h"
+#include "route_tail.h"
 
 namespace moe {
 namespace {
@@ -523,95 +524,14 @@ __global__ __launch_bounds__(1024) void route_select_kernel(RouteArgs a) {
 
 constexpr int kReduceThreads = 512;  // 8 waves, one expert each
 
-__device__ double block_sum(double v, double* sh) {
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  for (int s = kReduceThreads / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
-    __syncthreads();
-  }
-  const double r = sh[0];
-  __syncthreads();
-  return r;
-}
-
-// One block of kReduceThreads: switch loss and the two CV^2 values from the
-// per-expert sums (fixed order).
-__device__ void aux_block(const int32_t* __restrict__ counts_routed, const double* __restrict__ red, int E,
-                          int64_t T, int k, int noisy, float* __restrict__ aux_out, double* sh) {
-  double sw = 0.0, mi = 0.0, ml = 0.0;
-  for (int e = threadIdx.x; e < E; e += kReduceThreads) {
-    sw += ((double)counts_routed[e] / ((double)T * k)) * (red[e] / (double)T);
-    mi += red[E + e];
-    ml += red[2 * E + e];
-  }
-  sw = block_sum(sw, sh);
-  mi = block_sum(mi, sh) / E;
-  ml = block_sum(ml, sh) / E;
-  double vi = 0.0, vl = 0.0;
-  for (int e = threadIdx.x; e < E; e += kReduceThreads) {
-    const double di = red[E + e] - mi;
-    const double dl = red[2 * E + e] - ml;
-    vi += di * di;
-    vl += dl * dl;
-  }
-  vi = block_sum(vi, sh) / E;
-  vl = block_sum(vl, sh) / E;
-  if (threadIdx.x == 0) {
-    const float nan = __builtin_nanf("");
-    aux_out[0] = T > 0 ? (float)((double)E * sw) : nan;
-    aux_out[1] = T > 0 ? (E > 1 ? (float)(vi / (mi * mi)) : 0.0f) : nan;
-    aux_out[2] = (noisy && T > 0) ? (E > 1 ? (float)(vl / (ml * ml)) : 0.0f) : nan;
-  }
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;  // identical on every lane: each butterfly step adds the same two values
-}
-
 // Fixed-order sums (fp64) of the per-block partials, one expert per wave.
 __global__ __launch_bounds__(kReduceThreads) void route_reduce_kernel(
     const float* __restrict__ part_prob, const float* __restrict__ part_imp, const float* __restrict__ part_load,
     const int32_t* __restrict__ part_cnt, int nblk, int E, int32_t* __restrict__ counts_routed,
     double* __restrict__ red) {
-  const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * (kReduceThreads / 64) + (threadIdx.x >> 6);
   if (e >= E) return;
-  double p = 0.0, im = 0.0, ld = 0.0, cnt = 0.0;
-  constexpr int U = 8;  // loads of U rounds in flight together
-  for (int b0 = lane; b0 < nblk; b0 += 64 * U) {
-    float vp[U], vi[U], vl[U];
-    int32_t vc[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = b0 + 64 * u;
-      const int64_t o = (int64_t)e * nblk + (b < nblk ? b : 0);
-      vp[u] = part_prob[o];
-      vi[u] = part_imp[o];
-      vl[u] = part_load[o];
-      vc[u] = part_cnt[o];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (b0 + 64 * u >= nblk) break;
-      p += vp[u];
-      im += vi[u];
-      ld += vl[u];
-      cnt += vc[u];  // exact: integer-valued doubles far below 2^53
-    }
-  }
-  p = wave_sum_f64(p);
-  im = wave_sum_f64(im);
-  ld = wave_sum_f64(ld);
-  cnt = wave_sum_f64(cnt);
-  if (lane == 0) {
-    counts_routed[e] = (int32_t)cnt;
-    red[e] = p;
-    red[E + e] = im;
-    red[2 * E + e] = ld;
-  }
+  tail::reduce_expert(e, threadIdx.x & 63, part_prob, part_imp, part_load, part_cnt, nblk, E, counts_routed, red);
 }
 
 // One block: switch loss and the two CV^2 values from the per-expert sums.
@@ -619,7 +539,7 @@ __global__ __launch_bounds__(kReduceThreads) void route_aux_kernel(const int32_t
                                                                    const double* __restrict__ red, int E, int64_t T,
                                                                    int k, int noisy, float* __restrict__ aux_out) {
   __shared__ double sh[kReduceThreads];
-  aux_block(counts_routed, red, E, T, k, noisy, aux_out, sh);
+  tail::aux_block<kReduceThreads>(counts_routed, red, E, T, k, noisy, aux_out, sh);
 }
 
 __global__ void softplus_kernel(const float* __restrict__ z, float* __restrict__ out, int64_t n) {
@@ -733,6 +653,7 @@ hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
     err = noisy ? launch_select<true>(kk, ra, s) : launch_select<false>(kk, ra, s);
     if (err != hipSuccess) return err;
   }
+  if (a.defer_tail) return hipSuccess;
   hipLaunchKernelGGL(route_reduce_kernel, dim3((a.E + kReduceThreads / 64 - 1) / (kReduceThreads / 64)),
                      dim3(kReduceThreads), 0, s, a.part_prob, a.part_imp, a.part_load, a.part_cnt,
                      a.T > 0 ? nblk : 0, a.E, a.counts_routed, a.red);
