@@ -93,7 +93,11 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
       sc[e] += v;
       __syncthreads();
     }
-    if (e < E) tile_start[e] = (int32_t)(sc[e] - tiles);
+    if (e < E) {
+      const int32_t first = (int32_t)(sc[e] - tiles);
+      tile_start[e] = first;
+      for (int64_t j = 0; j < tiles; ++j) tile_start[E + 1 + first + j] = e;  // expert of each M-tile
+    }
     if (e == E - 1) tile_start[E] = (int32_t)sc[e];
   }
   // forward path: the balancing losses from the per-expert sums of the count kernel

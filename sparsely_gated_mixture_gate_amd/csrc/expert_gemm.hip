@@ -9,10 +9,12 @@
 //   H1[r] = act(Xp[r] . W1[e]),  Yp[r] = H1[r] . W2[e]   for r in segment e.
 //
 // Design (gfx950):
-//   * tile map: a one-block kernel turns offsets[E+1] into the prefix of
-//     ceil(rows_e / BM) M-tiles per expert; GEMM blocks binary-search it, so the
-//     host never synchronises on the ragged segment sizes. The grid is an upper
-//     bound (ceil(R_max / BM) + E M-tiles); surplus blocks exit at once.
+//   * tile map: a one-block kernel (in the forward path, the dispatch scan) turns
+//     offsets[E+1] into the prefix of ceil(rows_e / BM) M-tiles per expert and a
+//     table of the expert of every M-tile, so a GEMM block finds its tile with
+//     two dependent loads and the host never synchronises on the ragged segment
+//     sizes. The grid is an upper bound (ceil(R_max / BM) + E M-tiles); surplus
+//     blocks exit at once.
 //   * bf16 path: BM x BN x BK tiles, 512 threads = 2 x 4 waves of
 //     (BM/2) x (BN/4), MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation. Tile
 //     shape by the rows an expert can hold: capacity <= 160 -> 160 x 512 x 32
@@ -67,7 +69,10 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
     sc[e] += v;
     __syncthreads();
   }
-  if (e < E) tile_start[e] = sc[e] - tiles;
+  if (e < E) {
+    tile_start[e] = sc[e] - tiles;
+    for (int j = 0; j < tiles; ++j) tile_start[E + 1 + sc[e] - tiles + j] = e;  // expert of each M-tile
+  }
   if (e == E - 1) tile_start[E] = sc[e];
 }
 
@@ -113,11 +118,7 @@ __device__ __forceinline__ bool schedule_tile(const int32_t* __restrict__ tile_s
   const int L = (b % kXcds) * per + slot;
   if (slot >= per || L >= total) return false;
   const int mt_lin = L / nt_count;
-  int lo = 0, hi = E;  // tile_start[lo] <= mt_lin < tile_start[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tile_start[mid] <= mt_lin) lo = mid; else hi = mid;
-  }
+  const int lo = tile_start[E + 1 + mt_lin];  // the expert of M-tile mt_lin
   const int mt0 = tile_start[lo];
   const int mts = tile_start[lo + 1] - mt0;
   const int loc = L - mt0 * nt_count;

@@ -130,7 +130,10 @@ struct FfnWs {
 };
 FfnWs carve_ffn(Carver& c, const moe_params* p) {
   FfnWs w;
-  w.tile_start = c.take<int32_t>((size_t)p->E + 1);
+  // [E+1] M-tile prefix, then the expert of every M-tile (at most ceil(R / BM) + E tiles)
+  const int64_t bm = ffn_tile_rows(p->dtype, capacity_of(p), max_rows_of(p), p->E);
+  const int64_t mtiles = (max_rows_of(p) + bm - 1) / bm + p->E;
+  w.tile_start = c.take<int32_t>((size_t)p->E + 1 + (size_t)mtiles);
   w.h1 = c.take<char>((size_t)max_rows_of(p) * (size_t)p->d_ff * elt_size(p));
   return w;
 }
