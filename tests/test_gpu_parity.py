@@ -209,6 +209,7 @@ def _run_forward(moelib, c, dev, gate_mode=0):
     d = c["dev"]
     p = _params(moelib, c, gate_mode)
     fb = ForwardBuffers.alloc(p, dev)
+    fb.y.fill_(float("nan"))  # every row must be written (dropped tokens' rows as exact zeros)
     moelib.moe_forward(p, d["x"], d["w_gate"], d["gate_bias"], d["w_noise"], d["noise"], d["w1"], d["w2"], fb.y,
                        fb.aux, fb.topk_idx, fb.topk_gate, fb.counts_routed, fb.counts_kept, fb.slot_dest, fb.ws)
     torch.cuda.synchronize()
