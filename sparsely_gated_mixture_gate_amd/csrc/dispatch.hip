@@ -50,6 +50,23 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   for (int e = threadIdx.x; e < E; e += 256) blk_cnt[(int64_t)e * nb + blockIdx.x] = hist[e];
 }
 
+// Inclusive prefix sum over the 1024 threads of the block (shuffles inside each
+// wave, then the wave totals); sw holds 16 values.
+__device__ int64_t block_incl_scan(int64_t v, int64_t* sw) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) sw[wave] = v;
+  __syncthreads();
+  int64_t base = 0;
+  for (int w = 0; w < wave; ++w) base += sw[w];
+  __syncthreads();  // sw is reused by the next scan
+  return v + base;
+}
+
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ blk_cnt, int nb, int E,
                                                              int64_t C, int32_t* __restrict__ counts_kept,
                                                              int32_t* __restrict__ offsets,
@@ -57,8 +74,8 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
                                                              const int32_t* __restrict__ counts_routed,
                                                              const double* __restrict__ red, int64_t T, int k,
                                                              int noisy, float* __restrict__ aux_out) {
-  __shared__ int64_t sc[1024];
-  __shared__ double sh[1024];
+  __shared__ int64_t sw[16];
+  __shared__ double sh[16];
   const int e = threadIdx.x;
   int64_t run = 0;
   if (e < E) {
@@ -71,34 +88,19 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
   }
   const int64_t kept = (e < E) ? ((C >= 0 && run > C) ? C : run) : 0;
   if (e < E) counts_kept[e] = (int32_t)kept;
-  sc[e] = kept;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int64_t v = e >= off ? sc[e - off] : 0;
-    __syncthreads();
-    sc[e] += v;
-    __syncthreads();
-  }
-  if (e < E) offsets[e] = (int32_t)(sc[e] - kept);
-  if (e == E - 1) offsets[E] = (int32_t)sc[e];
+  const int64_t kept_incl = block_incl_scan(kept, sw);
+  if (e < E) offsets[e] = (int32_t)(kept_incl - kept);
+  if (e == E - 1) offsets[E] = (int32_t)kept_incl;
   if (tile_start) {
     // prefix of ceil(kept / tile_rows) M-tiles per expert for the expert FFN
     const int64_t tiles = (kept + tile_rows - 1) / tile_rows;
-    __syncthreads();
-    sc[e] = tiles;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int64_t v = e >= off ? sc[e - off] : 0;
-      __syncthreads();
-      sc[e] += v;
-      __syncthreads();
-    }
+    const int64_t tiles_incl = block_incl_scan(tiles, sw);
     if (e < E) {
-      const int32_t first = (int32_t)(sc[e] - tiles);
+      const int32_t first = (int32_t)(tiles_incl - tiles);
       tile_start[e] = first;
       for (int64_t j = 0; j < tiles; ++j) tile_start[E + 1 + first + j] = e;  // expert of each M-tile
     }
-    if (e == E - 1) tile_start[E] = (int32_t)sc[e];
+    if (e == E - 1) tile_start[E] = (int32_t)tiles_incl;
   }
   // forward path: the balancing losses from the per-expert sums of the count kernel
   if (aux_out) tail::aux_block<1024>(counts_routed, red, E, T, k, noisy, aux_out, sh);

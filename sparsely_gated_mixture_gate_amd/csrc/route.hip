@@ -538,7 +538,7 @@ __global__ __launch_bounds__(kReduceThreads) void route_reduce_kernel(
 __global__ __launch_bounds__(kReduceThreads) void route_aux_kernel(const int32_t* __restrict__ counts_routed,
                                                                    const double* __restrict__ red, int E, int64_t T,
                                                                    int k, int noisy, float* __restrict__ aux_out) {
-  __shared__ double sh[kReduceThreads];
+  __shared__ double sh[kReduceThreads / 64];
   tail::aux_block<kReduceThreads>(counts_routed, red, E, T, k, noisy, aux_out, sh);
 }
 

@@ -22,17 +22,17 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;  // identical on every lane: each butterfly step adds the same two values
 }
 
-// Sum over the NT threads of the block (tree order fixed by NT); sh holds NT doubles.
+// Sum over the NT threads of the block in a fixed order (butterfly inside each
+// wave, then the wave totals in wave order); sh holds NT / 64 doubles.
 template <int NT>
 __device__ double block_sum(double v, double* sh) {
-  sh[threadIdx.x] = v;
+  v = wave_sum_f64(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
-  for (int s = NT / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
-    __syncthreads();
-  }
-  const double r = sh[0];
-  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) r += sh[w];
+  __syncthreads();  // sh is reused by the next sum
   return r;
 }
 
@@ -79,7 +79,7 @@ __device__ __forceinline__ void reduce_expert(int e, int lane, const float* __re
 }
 
 // One block of NT threads: switch loss and the two CV^2 values from the
-// per-expert sums (fixed order); sh holds NT doubles.
+// per-expert sums (fixed order); sh holds NT / 64 doubles.
 template <int NT>
 __device__ void aux_block(const int32_t* __restrict__ counts_routed, const double* __restrict__ red, int E,
                           int64_t T, int k, int noisy, float* __restrict__ aux_out, double* sh) {
