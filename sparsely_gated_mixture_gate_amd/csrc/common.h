@@ -88,7 +88,9 @@ struct RouteLaunch {
   int32_t* part_cnt; // [E][nblk]
   double* red;       // [3][E]
 };
-int route_tokens_per_block(int E, bool noisy);
+// blocks of per-block partial sums the route writes (the gate kernels' grid)
+int route_partial_blocks(int64_t T, int E, int dtype, int gate_mode, bool logits_out);
+int route_fused_tokens(int64_t T);
 size_t route_weight_floats(int d, int E, bool noisy);
 size_t route_logit_floats(int64_t T, int E, bool noisy);
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s);

@@ -104,8 +104,7 @@ struct RouteWs {
   double* red;
 };
 RouteWs carve_route(Carver& c, const moe_params* p, bool noisy) {
-  const int tpb = route_tokens_per_block(p->E, noisy);
-  const int64_t nblk = (p->T + tpb - 1) / tpb;
+  const int64_t nblk = (p->T + 31) / 32;  // the most partial-sum blocks any gate path writes (32-token blocks)
   const size_t n = (size_t)p->E * (size_t)(nblk > 0 ? nblk : 1);
   RouteWs w;
   w.wc = c.take<float>(route_weight_floats(p->d_model, p->E, noisy));
@@ -268,7 +267,7 @@ moe_status run_dispatch(const moe_params* p, const void* x, const int32_t* topk_
   a.part_imp = route_tail ? route_tail->part_imp : nullptr;
   a.part_load = route_tail ? route_tail->part_load : nullptr;
   a.part_cnt = route_tail ? route_tail->part_cnt : nullptr;
-  a.route_nblk = p->T > 0 ? (int)((p->T + route_tokens_per_block(p->E, noisy) - 1) / route_tokens_per_block(p->E, noisy)) : 0;
+  a.route_nblk = route_partial_blocks(p->T, p->E, p->dtype, p->gate_mode, false);
   a.counts_routed = counts_routed;
   a.red = route_tail ? route_tail->red : nullptr;
   a.aux_out = aux_out;

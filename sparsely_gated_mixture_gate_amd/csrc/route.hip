@@ -611,7 +611,12 @@ hipError_t launch_logits(const RouteLaunch& a, bool noisy, hipStream_t s) {
 }  // namespace
 }  // namespace moe
 
-int route_tokens_per_block(int E, bool noisy) { return 64; }
+int route_partial_blocks(int64_t T, int E, int dtype, int gate_mode, bool logits_out) {
+  if (T <= 0) return 0;
+  const bool fused = route_fused_supported(dtype, E) && gate_mode != 1 && !logits_out;
+  const int tpb = fused ? route_fused_tokens(T) : 64;
+  return (int)((T + tpb - 1) / tpb);
+}
 
 size_t route_weight_floats(int d, int E, bool noisy) { return (size_t)d * moe::route_ncol(E, noisy); }
 
@@ -620,7 +625,7 @@ size_t route_logit_floats(int64_t T, int E, bool noisy) { return (size_t)T * moe
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
   using namespace moe;
   const bool noisy = a.w_noise != nullptr;
-  const int nblk = (int)((a.T + 63) / 64);
+  const int nblk = route_partial_blocks(a.T, a.E, a.dtype, a.gate_mode, a.logits_out != nullptr);
   hipError_t err = hipSuccess;
   const bool fused = route_fused_supported(a.dtype, a.E) && a.gate_mode != 1 && a.logits_out == nullptr;
   if (a.T > 0 && fused) {
@@ -656,7 +661,7 @@ hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
   if (a.defer_tail) return hipSuccess;
   hipLaunchKernelGGL(route_reduce_kernel, dim3((a.E + kReduceThreads / 64 - 1) / (kReduceThreads / 64)),
                      dim3(kReduceThreads), 0, s, a.part_prob, a.part_imp, a.part_load, a.part_cnt,
-                     a.T > 0 ? nblk : 0, a.E, a.counts_routed, a.red);
+                     nblk, a.E, a.counts_routed, a.red);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.aux_out) {
     hipLaunchKernelGGL(route_aux_kernel, dim3(1), dim3(kReduceThreads), 0, s, a.counts_routed, a.red, a.E, a.T,

@@ -55,7 +55,7 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kTok = 64;     // tokens per block
+constexpr int kTok = 64;     // rows of the logit tile (a block routes 64 tokens, or 32)
 constexpr int kBK = 32;      // k per LDS stage (one MFMA k-step)
 
 // bf16 weight copy [d][ncol]: gate only: column c = expert c; noisy: block q of
@@ -119,7 +119,7 @@ __device__ __forceinline__ void wait_stages(int ld, int rem) {
 
 struct FusedArgs {
   int64_t T;
-  int d, E, k, renormalize, nblk, force_fallback, lpad;
+  int d, E, k, renormalize, nblk, force_fallback, lpad, tpb;
   const uint16_t* x;
   const uint16_t* wcat;
   const float* bias;
@@ -206,8 +206,10 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int d = a.d, E = a.E, k = a.k;
   const int64_t T = a.T;
-  const int64_t t0 = (int64_t)blockIdx.x * kTok;
-  const int rows = (int)min<int64_t>(kTok, T - t0);
+  // tokens t0 .. t0 + rows - 1 (a.tpb = 64, or 32 when 64-token blocks would leave
+  // CUs idle; the tile is 64 rows either way, rows past `rows` are clamped copies)
+  const int64_t t0 = (int64_t)blockIdx.x * a.tpb;
+  const int rows = (int)min<int64_t>(a.tpb, T - t0);
   if (tid < kTok) bmax_s[tid] = 0.0f;
 
   // ---- GEMM: V = x W and S = |x| |W| over the block's 64 tokens ----------------
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   if constexpr (NOISY) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const int64_t t = min<int64_t>(t0 + wm * (16 * MI) + mi * 16 + s, T - 1);
+      const int64_t t = t0 + min(wm * (16 * MI) + mi * 16 + s, rows - 1);
 #pragma unroll
       for (int ni = 0; ni < NE; ++ni) {
         const int e = 32 * wn + 16 * ni + 4 * g;
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
         if (e < EP) Hs[m * HS + e] = hv[j];
       }
       if constexpr (NOISY) {
-        if (t < T && e0 < E) {
+        if (m < rows && e0 < E) {
           if (e0 + 3 < E) {
             *reinterpret_cast<float4*>(a.CL + t * a.lpad + e0) = float4{clv[0], clv[1], clv[2], clv[3]};
             *reinterpret_cast<float4*>(a.SG + t * a.lpad + e0) = float4{spv[0], spv[1], spv[2], spv[3]};
@@ -481,7 +483,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
       if (q >= k) break;
       reinterpret_cast<int*>(rt)[4 + q] = sel_i[q];
       rt[12 + q] = gt[q];
-      if (t < T) {
+      if (tl < rows) {
         a.topk_idx[t * k + q] = sel_i[q];
         a.topk_gate[t * k + q] = gt[q];
       }
@@ -491,7 +493,6 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   // phase 2 (wave 0), lane = token: merge the 8 sorted lists and certify the
   // token; certified tokens get their results, the others return false
   auto merge = [&]() -> bool {
-    const int64_t t = t0 + lane;
     float sel_v[KK];
     int sel_i[KK];
     uint32_t heads = 0;  // 4 bits per list: index of its next candidate
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
       sel_v[r] = best;
       sel_i[r] = bi;
     }
-    if (t >= T) return true;  // rows past T: nothing to route
+    if (lane >= rows) return true;  // rows past the block's tokens: nothing to route
     bool ok = !a.force_fallback;
     const float b2 = 2.0f * bmax_s[lane];
     const int ngap = min(k, KK - 1);
@@ -841,6 +842,20 @@ size_t route_wcat_elems(int d, int E, bool noisy) {
   return (size_t)d * moe::fused_ep(E) * (noisy ? 2 : 1);
 }
 
+// Tokens per block of the certified gate: a block holds most of a CU's LDS, so
+// when 64-token blocks would leave CUs idle the blocks take 32 tokens.
+int route_fused_tokens(int64_t T) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    cus = (hipGetDevice(&dev) == hipSuccess &&
+           hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+              ? n
+              : 256;
+  }
+  return (T + 63) / 64 < cus ? 32 : 64;
+}
+
 hipError_t launch_route_fused(const RouteLaunch& a, bool noisy, int force_fallback, float* CL, float* SG, int lpad,
                               hipStream_t s) {
   using namespace moe;
@@ -863,7 +878,8 @@ hipError_t launch_route_fused(const RouteLaunch& a, bool noisy, int force_fallba
   fa.E = a.E;
   fa.k = a.k;
   fa.renormalize = a.renormalize;
-  fa.nblk = (int)((a.T + kTok - 1) / kTok);
+  fa.tpb = route_fused_tokens(a.T);
+  fa.nblk = (int)((a.T + fa.tpb - 1) / fa.tpb);
   fa.force_fallback = force_fallback;
   fa.lpad = lpad;
   fa.x = static_cast<const uint16_t*>(a.x);
