@@ -77,13 +77,29 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
   __shared__ int64_t sw[16];
   __shared__ double sh[16];
   const int e = threadIdx.x;
+  // inputs of the losses (forward path), loaded now so they arrive during the scans
+  int32_t cr_e = 0;
+  double r0 = 0.0, r1 = 0.0, r2 = 0.0;
+  if (aux_out && e < E) {
+    cr_e = counts_routed[e];
+    r0 = red[e];
+    r1 = red[E + e];
+    r2 = red[2 * E + e];
+  }
+  // exclusive prefix of the block counts along expert e's row, 8 loads in flight
   int64_t run = 0;
   if (e < E) {
     int32_t* row = blk_cnt + (int64_t)e * nb;
-    for (int b = 0; b < nb; ++b) {
-      const int32_t c = row[b];
-      row[b] = (int32_t)run;
-      run += c;
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      int32_t c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = b0 + u < nb ? row[b0 + u] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b0 + u < nb) {
+          row[b0 + u] = (int32_t)run;
+          run += c[u];
+        }
     }
   }
   const int64_t kept = (e < E) ? ((C >= 0 && run > C) ? C : run) : 0;
@@ -103,18 +119,102 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
     if (e == E - 1) tile_start[E] = (int32_t)tiles_incl;
   }
   // forward path: the balancing losses from the per-expert sums of the count kernel
-  if (aux_out) tail::aux_block<1024>(counts_routed, red, E, T, k, noisy, aux_out, sh);
+  if (aux_out) tail::aux_from_values<1024>(e < E, cr_e, r0, r1, r2, E, T, k, noisy, aux_out, sh);
 }
 
+// SCAN = false: blk_base holds the exclusive prefixes of the block counts along
+// each expert and offsets the segment starts (written by the scan kernel).
+// SCAN = true (small count tables): blk_base holds the raw block counts; every
+// block derives its own prefixes and the offsets from them, and block 0 also
+// writes counts_kept, offsets, the FFN tile map and the losses (as the scan
+// kernel would), so no separate scan launch is needed.
+template <bool SCAN>
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __restrict__ idx, int64_t n, int k,
                                                             int E, int nbits, int nb, int64_t C,
                                                             const int32_t* __restrict__ blk_base,
                                                             const int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ slot_dest,
                                                             int32_t* __restrict__ row_src,
-                                                            uint4* __restrict__ y_zero, int y_chunks) {
-  extern __shared__ int wcnt[];  // [4 waves][E] running counts
+                                                            uint4* __restrict__ y_zero, int y_chunks,
+                                                            const DispatchLaunch so) {
+  extern __shared__ int wcnt[];  // [4 waves][E] running counts; SCAN: then base [E], segment starts [E + 1]
   for (int i = threadIdx.x; i < 4 * E; i += 256) wcnt[i] = 0;
+  int* const base_s = wcnt + 4 * E;
+  int* const off_s = base_s + E;
+  if constexpr (SCAN) {
+    __shared__ int64_t sw[16];
+    __shared__ double sh[16];
+    // per expert: counts of the blocks before this one, and the total
+    for (int e = threadIdx.x; e < E; e += 256) {
+      const int32_t* row = blk_base + (int64_t)e * nb;
+      int before = 0, tot = 0;
+      for (int b0 = 0; b0 < nb; b0 += 8) {
+        int32_t c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = b0 + u < nb ? row[b0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          before += b0 + u < (int)blockIdx.x ? c[u] : 0;
+          tot += c[u];
+        }
+      }
+      base_s[e] = before;
+      off_s[e] = (C >= 0 && tot > C) ? (int)C : tot;  // kept rows, turned into segment starts below
+    }
+    __syncthreads();
+    // segment starts: exclusive prefix of the kept rows over the experts (thread t: experts 4t .. 4t+3)
+    int kept4[4];
+    int64_t loc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * (int)threadIdx.x + j;
+      kept4[j] = e < E ? off_s[e] : 0;
+      loc += kept4[j];
+    }
+    const int64_t incl = block_incl_scan(loc, sw);
+    __syncthreads();
+    int64_t run = incl - loc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * (int)threadIdx.x + j;
+      if (e < E) off_s[e] = (int)run;
+      run += kept4[j];
+    }
+    if (threadIdx.x == 255) off_s[E] = (int)incl;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int e = threadIdx.x; e <= E; e += 256) so.offsets[e] = off_s[e];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = 4 * (int)threadIdx.x + j;
+        if (e < E) so.counts_kept[e] = kept4[j];
+      }
+      if (so.tile_start) {
+        // prefix of ceil(kept / tile_rows) M-tiles per expert, and the expert of each M-tile
+        int tiles4[4];
+        int64_t tl = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          tiles4[j] = (kept4[j] + so.tile_rows - 1) / so.tile_rows;
+          tl += tiles4[j];
+        }
+        const int64_t tincl = block_incl_scan(tl, sw);
+        int64_t first = tincl - tl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * (int)threadIdx.x + j;
+          if (e < E) {
+            so.tile_start[e] = (int32_t)first;
+            for (int q = 0; q < tiles4[j]; ++q) so.tile_start[E + 1 + first + q] = e;
+          }
+          first += tiles4[j];
+        }
+        if (threadIdx.x == 255) so.tile_start[E] = (int32_t)tincl;
+      }
+      if (so.route_tail && so.aux_out)
+        tail::aux_block<256>(so.counts_routed, so.red, E, so.T, so.k, so.noisy, so.aux_out, sh);
+    }
+  }
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -148,10 +248,10 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
     dropped[q] = false;
     if (e < 0) continue;
     const int64_t a = base + q * 64 + lane;
-    int64_t r = (int64_t)blk_base[(int64_t)e * nb + blockIdx.x] + loc[q];
+    int64_t r = (SCAN ? (int64_t)base_s[e] : (int64_t)blk_base[(int64_t)e * nb + blockIdx.x]) + loc[q];
     for (int w = 0; w < wave; ++w) r += wcnt[w * E + e];
     const bool keep = C < 0 || r < C;
-    const int32_t slot = keep ? (int32_t)(offsets[e] + r) : -1;
+    const int32_t slot = keep ? (int32_t)((SCAN ? off_s[e] : offsets[e]) + r) : -1;
     slot_dest[a] = slot;
     if (keep) row_src[slot] = (int32_t)(a / k);
     dropped[q] = !keep;
@@ -202,16 +302,27 @@ hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s) {
                        nb, a.blk_cnt, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, a.blk_cnt, nb, a.E, a.C, a.counts_kept,
-                     a.offsets, a.tile_start, a.tile_rows, a.counts_routed, a.red, a.T, a.k, a.noisy,
-                     a.route_tail ? a.aux_out : nullptr);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // small count tables: every rank block derives its own prefixes (no scan launch)
+  const bool scan_in_rank = nb > 0 && (int64_t)nb * a.E <= 16384;
+  if (!scan_in_rank) {
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, a.blk_cnt, nb, a.E, a.C, a.counts_kept,
+                       a.offsets, a.tile_start, a.tile_rows, a.counts_routed, a.red, a.T, a.k, a.noisy,
+                       a.route_tail ? a.aux_out : nullptr);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if (nb == 0) return hipSuccess;
   int nbits = 0;
   while ((1 << nbits) < a.E) ++nbits;
-  hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nb), dim3(256), sizeof(int) * 4 * a.E, s, a.topk_idx, n, a.k, a.E,
-                     nbits, nb, a.C, a.blk_cnt, a.offsets, a.slot_dest, a.row_src, static_cast<uint4*>(a.y_zero),
-                     a.d * (a.dtype == 1 ? 2 : 4) / 16);
+  const int y_chunks = a.d * (a.dtype == 1 ? 2 : 4) / 16;
+  if (scan_in_rank) {
+    hipLaunchKernelGGL(dispatch_rank_kernel<true>, dim3(nb), dim3(256), sizeof(int) * (6 * a.E + 1), s, a.topk_idx,
+                       n, a.k, a.E, nbits, nb, a.C, a.blk_cnt, a.offsets, a.slot_dest, a.row_src,
+                       static_cast<uint4*>(a.y_zero), y_chunks, a);
+  } else {
+    hipLaunchKernelGGL(dispatch_rank_kernel<false>, dim3(nb), dim3(256), sizeof(int) * 4 * a.E, s, a.topk_idx, n,
+                       a.k, a.E, nbits, nb, a.C, a.blk_cnt, a.offsets, a.slot_dest, a.row_src,
+                       static_cast<uint4*>(a.y_zero), y_chunks, a);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int elt = a.dtype == 1 ? 2 : 4;
   const int cpr = a.d * elt / 16;

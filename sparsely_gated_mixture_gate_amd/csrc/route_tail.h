@@ -78,6 +78,25 @@ __device__ __forceinline__ void reduce_expert(int e, int lane, const float* __re
   }
 }
 
+// The same from values already in registers, for E <= NT: thread e (have = e < E)
+// holds counts_routed[e] and the three sums of expert e.
+template <int NT>
+__device__ void aux_from_values(bool have, int32_t cr, double r0, double r1, double r2, int E, int64_t T, int k,
+                                int noisy, float* __restrict__ aux_out, double* sh) {
+  const double sw = block_sum<NT>(have ? ((double)cr / ((double)T * k)) * (r0 / (double)T) : 0.0, sh);
+  const double mi = block_sum<NT>(have ? r1 : 0.0, sh) / E;
+  const double ml = block_sum<NT>(have ? r2 : 0.0, sh) / E;
+  const double di = r1 - mi, dl = r2 - ml;
+  const double vi = block_sum<NT>(have ? di * di : 0.0, sh) / E;
+  const double vl = block_sum<NT>(have ? dl * dl : 0.0, sh) / E;
+  if (threadIdx.x == 0) {
+    const float nan = __builtin_nanf("");
+    aux_out[0] = T > 0 ? (float)((double)E * sw) : nan;
+    aux_out[1] = T > 0 ? (E > 1 ? (float)(vi / (mi * mi)) : 0.0f) : nan;
+    aux_out[2] = (noisy && T > 0) ? (E > 1 ? (float)(vl / (ml * ml)) : 0.0f) : nan;
+  }
+}
+
 // One block of NT threads: switch loss and the two CV^2 values from the
 // per-expert sums (fixed order); sh holds NT / 64 doubles.
 template <int NT>

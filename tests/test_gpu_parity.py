@@ -210,6 +210,7 @@ def _run_forward(moelib, c, dev, gate_mode=0):
     p = _params(moelib, c, gate_mode)
     fb = ForwardBuffers.alloc(p, dev)
     fb.y.fill_(float("nan"))  # every row must be written (dropped tokens' rows as exact zeros)
+    fb.aux.fill_(float("nan"))  # aux has 3 values; the 4th (alignment padding) is never written
     moelib.moe_forward(p, d["x"], d["w_gate"], d["gate_bias"], d["w_noise"], d["noise"], d["w1"], d["w2"], fb.y,
                        fb.aux, fb.topk_idx, fb.topk_gate, fb.counts_routed, fb.counts_kept, fb.slot_dest, fb.ws)
     torch.cuda.synchronize()
@@ -262,6 +263,8 @@ SMALL = [
     ("dropless_top1", dict(T=999, d_model=512, d_ff=640)),
     # 256-row expert tiles: ragged K and N, more tiles than CUs (several per persistent block)
     ("dropless_top1", dict(T=40000, E=4, d_model=200, d_ff=328)),
+    # count table too large for in-block prefixes (separate scan kernel)
+    ("noisy_top4", dict(T=5000, E=512, k=8, d_model=64, d_ff=64)),
     # 256-row tiles with a capacity between 160 and 256 (row tiles past the segment skipped)
     ("gshard_top2", dict(T=4000, E=16, capacity=200, d_model=296, d_ff=520)),
 ]
