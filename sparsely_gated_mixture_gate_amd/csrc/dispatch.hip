@@ -8,16 +8,22 @@
 // walking tokens in order (slots in order within a token), each assignment
 // takes the next rank of its expert and is kept iff rank < C.
 //
-// Design (gfx950), four launches, all integer work exact and deterministic:
+// Design (gfx950), up to four launches, all integer work exact and deterministic:
 //   count   per 1024-assignment block, per-expert counts (LDS integer atomics);
+//           in the forward path extra blocks also reduce the gate's per-block
+//           partial sums (one expert per wave);
 //   scan    one block: for each expert, exclusive prefix over blocks (the
 //           block's base rank), kept = min(count, C), offsets = exclusive
-//           prefix over experts;
+//           prefix over experts, the expert FFN's tile map, the losses. Not
+//           launched when blocks x experts <= 16384: then every rank block
+//           derives its own base ranks and the offsets from the raw counts;
 //   rank    per block: stable ranks inside each wave from 64-lane ballots on
 //           the bits of the expert id (multisplit), per-wave running counts in
-//           LDS, then base + earlier waves + in-wave rank -> slot or -1;
+//           LDS, then base + earlier waves + in-wave rank -> slot or -1; top-1
+//           forward path: zero the output rows of dropped tokens;
 //   permute one 16-byte chunk per thread: x_perm[r] = x[row_src[r]], reads of
-//           whole rows, fully coalesced writes.
+//           whole rows, fully coalesced writes (not needed by the bf16 forward
+//           path, whose expert GEMM gathers its rows from x).
 #include "common.h"
 #include "route_tail.h"
 

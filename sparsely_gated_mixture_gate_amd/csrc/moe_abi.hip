@@ -159,8 +159,11 @@ ForwardWs carve_forward(Carver& c, const moe_params* p, bool noisy) {
   w.offsets = c.take<int32_t>((size_t)p->E + 1);
   w.slot_dest = c.take<int32_t>(tk);
   w.row_src = c.take<int32_t>(rows);
-  w.x_perm = c.take<char>(rows * (size_t)p->d_model * elt_size(p));
-  w.y_perm = c.take<char>(rows * (size_t)p->d_model * elt_size(p));
+  // bf16: the expert GEMM gathers its rows from x (no x_perm) and, for top-1 layers,
+  // writes y directly (no y_perm)
+  const bool bf16 = p->dtype == MOE_BF16;
+  w.x_perm = bf16 ? nullptr : c.take<char>(rows * (size_t)p->d_model * elt_size(p));
+  w.y_perm = (bf16 && p->k == 1) ? nullptr : c.take<char>(rows * (size_t)p->d_model * elt_size(p));
   return w;
 }
 
