@@ -37,8 +37,9 @@ __device__ __forceinline__ float activation(float z) {
 // either sign of z (z - h for z >= 0, -h = z q / 2 for z < 0), so there is no
 // cancellation for negative z. The 1/2 is folded into the coefficients of P. |z|
 // is clamped at 10 inside h (h < 1e-20 there), which keeps infinite z finite.
+// Both clamps are single v_med3_f32 (fminf / fmaxf would add canonicalising ops).
 __device__ __forceinline__ float gelu_fast(float z) {
-  const float za = fminf(fabsf(z), 10.0f);
+  const float za = __builtin_amdgcn_fmed3f(fabsf(z), 0.0f, 10.0f);
   const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f * 0.70710678118654752f, za, 1.0f));
   float r = __builtin_fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
   r = __builtin_fmaf(r, t, 0.5f * 1.421413741f);
@@ -46,13 +47,13 @@ __device__ __forceinline__ float gelu_fast(float z) {
   r = __builtin_fmaf(r, t, 0.5f * 0.254829592f);
   r = r * t;
   const float e = __builtin_amdgcn_exp2f(za * (za * (-0.5f * 1.4426950408889634f)));
-  return __builtin_fmaf(-(za * r), e, fmaxf(z, 0.0f));
+  return __builtin_fmaf(-(za * r), e, __builtin_amdgcn_fmed3f(z, 0.0f, 3.40282347e38f));
 }
 
 template <int ACT>
 __device__ __forceinline__ float activation_bf16(float z) {
   if constexpr (ACT == 0) {
-    return z > 0.0f ? z : 0.0f;
+    return __builtin_amdgcn_fmed3f(z, 0.0f, 3.40282347e38f);  // max(z, 0) in one op
   } else {
     return gelu_fast(z);
   }

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
                                                                 const int32_t* __restrict__ c_map,
                                                                 const float* __restrict__ c_scale) {
   // a_map (or null): A row r of a segment is row a_map[r] of the a_rows-row buffer A.
-  // c_map (or null): C row r is written to row c_map[r], scaled by c_scale[c_map[r]].
+  // c_map (or null; layer 2 only): C row r is written to row c_map[r], scaled by c_scale[c_map[r]].
   constexpr int NT = 64 * NW;            // threads
   constexpr int WN_W = BN / WNT;         // waves along N
   constexpr int WM_W = NW / WN_W;        // waves along M
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
     orow_m[mi] = 0;
     scale_m[mi] = 1.0f;
   }
-  if (c_map) {
+  if (!APPLY_ACT && c_map) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       const int grow = row0 + (wave / WN_W) * WM + mi * 16 + (tid & 15);
@@ -260,7 +260,11 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const uint32_t dst = lds0 + (uint32_t)((st * STAGE_CH + A_CH + i * NT + wave * 64) * 16);
-      load_to_lds(__builtin_amdgcn_readfirstlane(dst), last ? voffB_last[i] : voffB[i], rsB, soffB);
+      // SKIP: one M-tile per expert, so each weight byte is read by this workgroup only
+      if constexpr (SKIP)
+        load_to_lds_nt(__builtin_amdgcn_readfirstlane(dst), last ? voffB_last[i] : voffB[i], rsB, soffB);
+      else
+        load_to_lds(__builtin_amdgcn_readfirstlane(dst), last ? voffB_last[i] : voffB[i], rsB, soffB);
     }
   };
 
@@ -408,7 +412,7 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
   for (int mi = 0; mi < MI; ++mi) {
     const int grow = row0 + wm * WM + mi * 16 + s;
     if (grow >= row_end) continue;
-    const int64_t orow = c_map ? orow_m[mi] : grow;
+    const int64_t orow = (!APPLY_ACT && c_map) ? orow_m[mi] : grow;
     const float scale = scale_m[mi];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
@@ -417,8 +421,9 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
       float v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[j] = APPLY_ACT ? activation_bf16<ACT>(acc[mi][ni][j]) : acc[mi][ni][j];
-        if (c_map) v[j] = scale * v[j];
+        // layer 1 never scatters; in layer 2 the scale is 1 unless rows are scattered
+        if constexpr (APPLY_ACT) v[j] = activation_bf16<ACT>(acc[mi][ni][j]);
+        else v[j] = scale * acc[mi][ni][j];
       }
       uint2 o;
       o.x = pack_bf16x2(v[0], v[1]);

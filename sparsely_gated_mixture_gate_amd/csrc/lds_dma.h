@@ -33,6 +33,16 @@ __device__ __forceinline__ void load_to_lds(uint32_t lds_base, int voffset, cons
                : "memory", "m0");
 }
 
+// The same load with the non-temporal hint, for data that this workgroup alone
+// reads once (a weight panel streamed by exactly one tile): the hint keeps it from
+// displacing reused lines in the caches.
+__device__ __forceinline__ void load_to_lds_nt(uint32_t lds_base, int voffset, const int32x4& rsrc, int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
+               : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N) (expcnt / lgkmcnt not waited).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
