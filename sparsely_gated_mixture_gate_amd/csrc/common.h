@@ -37,7 +37,9 @@ __device__ __forceinline__ float activation(float z) {
 // either sign of z (z - h for z >= 0, -h = z q / 2 for z < 0), so there is no
 // cancellation for negative z. The 1/2 is folded into the coefficients of P. |z|
 // is clamped at 10 inside h (h < 1e-20 there), which keeps infinite z finite.
-// Both clamps are single v_med3_f32 (fminf / fmaxf would add canonicalising ops).
+// Both clamps are single v_med3_f32 (fminf / fmaxf would add canonicalising ops);
+// the upper bound FLT_MAX of max(z, 0) turns +inf into FLT_MAX, which the bf16
+// rounding of the output takes back to +inf.
 __device__ __forceinline__ float gelu_fast(float z) {
   const float za = __builtin_amdgcn_fmed3f(fabsf(z), 0.0f, 10.0f);
   const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f * 0.70710678118654752f, za, 1.0f));
@@ -53,7 +55,7 @@ __device__ __forceinline__ float gelu_fast(float z) {
 template <int ACT>
 __device__ __forceinline__ float activation_bf16(float z) {
   if constexpr (ACT == 0) {
-    return __builtin_amdgcn_fmed3f(z, 0.0f, 3.40282347e38f);  // max(z, 0) in one op
+    return __builtin_amdgcn_fmed3f(z, 0.0f, 3.40282347e38f);  // max(z, 0) in one op (+inf: as in gelu_fast)
   } else {
     return gelu_fast(z);
   }

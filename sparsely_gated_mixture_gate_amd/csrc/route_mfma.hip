@@ -192,6 +192,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   __shared__ float bmax_s[kTok];
   __shared__ int flist_s[kTok];
   __shared__ int nflag_s;
+  __shared__ int fb_full_s;  // the candidate pairs do not fit: the block recomputes whole rows
+  __shared__ int np_s;       // candidate pairs of the block
   char* smem = reinterpret_cast<char*>(smem_u4);
   float* Hs = reinterpret_cast<float*>(smem);
   float* cand_v = reinterpret_cast<float*>(smem + OFF_CV);
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   const int64_t t0 = (int64_t)blockIdx.x * a.tpb;
   const int rows = (int)min<int64_t>(a.tpb, T - t0);
   if (tid < kTok) bmax_s[tid] = 0.0f;
+  if (tid == 0) fb_full_s = 0;
 
   // ---- GEMM: V = x W and S = |x| |W| over the block's 64 tokens ----------------
   const int32x4 rsX = buffer_rsrc(a.x + t0 * d, (uint32_t)rows * d * 2);
@@ -523,7 +526,11 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
 #pragma unroll
     for (int r = 0; r + 1 < KK; ++r)
       if (r < ngap) ok = ok && (sel_v[r] - sel_v[r + 1] > b2);  // false for NaN
-    if (!ok) return false;
+    if (!ok) {
+      // candidates of the canonical top-KK: every expert with v >= v_KK - 2B (see the fallback)
+      res[lane * RS + 20] = sel_v[KK - 1] - b2;
+      return false;
+    }
     float m = -INFINITY;
     for (int w = 0; w < 8; ++w) m = fmaxf(m, wmax[w * 64 + lane]);
     float S = 0.0f;
@@ -596,142 +603,287 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   // tokens' x chunks stream through a 2-stage LDS ring (direct-to-LDS loads).
   const int nflag = nflag_s;
   if (nflag > 0) {
-    constexpr int TPR = 512 / NCOL;  // token slots
-    constexpr int NFG = FR / TPR;    // tokens per thread
-    const int f0 = tid / NCOL, c = tid % NCOL;
-    const int32x4 rsXall = buffer_rsrc(a.x, (uint32_t)(T * d * 2));
-    const uint32_t fl0 = lds_address(&smem_u4[OFF_CV / 16]);
-    uint32_t fvoff[F_NR];  // byte offsets (x offsets can pass 2^31; T*d*2 < 2^32 is checked on the host)
-    bool fisW[F_NR], fact[F_NR];
-    int fld = 0;
+    // A flagged token's canonical logit c_e lies within B (its largest bound) of the
+    // MFMA value v_e. With V the KK-th largest v, the KK experts with v >= V have
+    // c >= V - B, so an expert with v_e < V - 2B has c_e < V - B and cannot be in
+    // the canonical top-KK. Only the other experts (the candidates) need their
+    // canonical chains; the rest keep their MFMA logits, which then enter only the
+    // softmax sums. The (token, candidate) pairs are listed in token order, their
+    // x rows and weight columns gathered into LDS as fp32 by all threads, and each
+    // chain run by one thread from LDS (one fma per step), in rounds of as many
+    // pairs as the LDS holds. The
+    // forced fallback, and blocks with more pairs than threads (or than 16 rounds),
+    // recompute whole rows instead (below).
+    int* pair_tok = reinterpret_cast<int*>(smem + OFF_CV);  // [512] token row of each pair
+    int* pair_e = pair_tok + 512;                            // [512] its expert
+    constexpr int OFF_ST = OFF_CV + 4096;                    // staged operands, one block per pair
+    static_assert(OFF_WM - OFF_CV >= 4096 && SMEM >= OFF_ST, "candidate lists");
+    constexpr int NROW = NOISY ? 3 : 2;                      // x row, gate column (, noise column)
+    // pair block: NROW rows of d floats, padded to 4 dwords mod 64 so that the
+    // chains' 16-byte reads (one pair per lane) fall on distinct banks
+    const int pb_dw = NROW * d;
+    const int pb = 4 * (pb_dw + ((4 - pb_dw % 64) + 64) % 64);
+    const int maxp = (SMEM - OFF_ST) / pb;
+    int* resi = reinterpret_cast<int*>(res);
+    // candidates of flagged token q (lane = expert), in expert order; with emit, their
+    // pairs are written from the token's list offset on; returns the count
+    auto candidates = [&](int q, bool emit) -> int {
+      const int m = flist_s[q];
+      const float lo = res[m * RS + 20];
+      const float* hrow = Hs + m * HS;
+      int cnt = emit ? resi[m * RS + 22] : 0;
+      const int c0 = cnt;
 #pragma unroll
-    for (int i = 0; i < F_NR; ++i) {
-      fact[i] = (i * 512 + wave * 64) < F_CH;  // wave-uniform (the x chunks may fill part of a wave)
-      fisW[i] = (i * 512 + wave * 64) < F_WCH;
-      fld += fact[i] ? 1 : 0;
-      const int cc = tid + 512 * i;
-      const int kr = cc / BCR, p = cc % BCR;
-      fvoff[i] = (uint32_t)(kr * NCOL * 2 + ((p ^ swz_w<BCR>(kr)) << 4));  // weight chunks (x chunks set per round)
+      for (int c = 0; c < EP / 64; ++c) {
+        const int e = lane + 64 * c;
+        const bool cand = e < E && !(hrow[e] < lo);  // a NaN logit or bound makes a candidate
+        const uint64_t bal = __ballot(cand);
+        if (emit && cand) {
+          const int pos =
+              cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          pair_tok[pos] = m;
+          pair_e[pos] = e;
+        }
+        cnt += __popcll(bal);
+      }
+      return cnt - c0;
+    };
+    bool full = a.force_fallback != 0 || maxp < 1;
+    if (!full) {
+      for (int q = wave; q < nflag; q += 8) {
+        const int cnt = candidates(q, false);
+        if (lane == 0) resi[flist_s[q] * RS + 21] = cnt;
+      }
+      __syncthreads();
+      if (wave == 0) {  // list offsets in token order
+        const int c = lane < nflag ? resi[flist_s[lane] * RS + 21] : 0;
+        int v = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int n = __shfl_up(v, off);
+          if (lane >= off) v += n;
+        }
+        if (lane < nflag) resi[flist_s[lane] * RS + 22] = v - c;
+        if (lane == 63) {
+          np_s = v;
+          fb_full_s = (v > 512 || v > 16 * maxp) ? 1 : 0;
+        }
+      }
+      __syncthreads();
+      full = fb_full_s != 0;
     }
-    // One round: NF tokens per thread (TPR * NF tokens), chains interleaved over
-    // the tokens so consecutive fmas are independent.
-    auto round = [&](int base, auto nf_tag) {
-      constexpr int NF = decltype(nf_tag)::value;
-      constexpr int RT = TPR * NF;  // tokens in this round
-      // x chunk slots: row r of the round (token flist[base + r], or a valid row), chunk p
+    if (!full) {
+      const int np = np_s;
+      for (int q = wave; q < nflag; q += 8) candidates(q, true);
+      __syncthreads();
+      const int n8 = d / 8;
+      for (int p0 = 0; p0 < np; p0 += maxp) {
+        const int pr = min(maxp, np - p0);
+        // gather: item (pair, 8 consecutive k) -> one 16-byte x load and 8 (16) weight
+        // loads, widened to fp32
+        auto gather = [&](int it) {
+          const int pl = it / n8, j8 = it - (it / n8) * n8;
+          const int m = pair_tok[p0 + pl], e = pair_e[p0 + pl];
+          float* blk = reinterpret_cast<float*>(smem + OFF_ST + pl * pb) + 8 * j8;
+          const uint4 xv = *reinterpret_cast<const uint4*>(a.x + (t0 + m) * d + 8 * j8);
+          const uint16_t* __restrict__ w = a.wcat + (size_t)(8 * j8) * NCOL + (NOISY ? 64 * (e >> 5) + (e & 31) : e);
+          uint32_t wg[8], wn[8];
 #pragma unroll
-      for (int i = 0; i < F_NR; ++i) {
-        const int cc = tid + 512 * i - F_WCH;
-        if (cc >= 0) {
-          const int r = min(cc / F_CPR, FR - 1), p = cc % F_CPR;  // lanes past the x chunks: any valid offset
-          const int m = flist_s[min(base + r, nflag - 1)];
-          fvoff[i] = (uint32_t)((t0 + m) * d * 2) + (uint32_t)(p << 4);
-        }
-      }
-      auto fissue = [&](int kt) {
-        const int st = kt % F_STAGES;
-#pragma unroll
-        for (int i = 0; i < F_NR; ++i) {
-          if (!fact[i]) continue;
-          const uint32_t dst = fl0 + (uint32_t)((st * F_CH + i * 512 + wave * 64) * 16);
-          if (fisW[i]) {
-            load_to_lds(__builtin_amdgcn_readfirstlane(dst), (int)(fvoff[i] + (uint32_t)(kt * F_BK * NCOL * 2)), rsW, 0);
-          } else if (tid + 512 * i < F_CH) {  // x chunks: every slot loads (slots past this round's rows repeat a
-                                               // valid row), so every wave with fact[i] issues the load its waits count
-            load_to_lds(__builtin_amdgcn_readfirstlane(dst), (int)(fvoff[i] + (uint32_t)(kt * F_BK * 2)), rsXall, 0);
+          for (int u = 0; u < 8; ++u) {
+            wg[u] = w[(size_t)u * NCOL];
+            if constexpr (NOISY) wn[u] = w[(size_t)u * NCOL + 32];
           }
-        }
-      };
-      float accv[NF];
+          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-      for (int q = 0; q < NF; ++q) accv[q] = 0.0f;
-      const bool busy = base + f0 * NF < nflag;  // wave-uniform (a wave's columns share one token slot)
-      const int fnk = (d + F_BK - 1) / F_BK;
-#pragma unroll
-      for (int t = 0; t < F_STAGES - 1; ++t)
-        if (t < fnk) fissue(t);
-      for (int kt = 0; kt < fnk; ++kt) {
-        wait_stages<F_STAGES - 2>(fld, min(F_STAGES - 2, fnk - 1 - kt));
-        block_barrier();  // stage kt in LDS for every wave; the buffer of stage kt-1 is free
-        if (kt + F_STAGES - 1 < fnk) fissue(kt + F_STAGES - 1);
-        const char* sb = smem + OFF_CV + (kt % F_STAGES) * F_CH * 16;
-        lds_char* sw = (lds_char*)(&smem_u4[OFF_CV / 16 + (kt % F_STAGES) * F_CH]);
-        const uint4* sx = reinterpret_cast<const uint4*>(sb + F_WCH * 16);
-        const int nj = min(F_BK, d - kt * F_BK);  // a multiple of 8
-        auto do_q8 = [&](int q8) {
-          // column c's weights of rows 8 q8 .. +7 by two transposing reads: the lanes
-          // of a 16-lane group hold 16 consecutive columns, source lane s points at
-          // row 8 q8 + s/4, columns 4 (s%4) .. +3 of the group
-          const int kr = q8 * 8 + ((lane & 15) >> 2);
-          const int nc = (c - lane) + 16 * (lane >> 4) + 4 * (lane & 3);
-          const int b0 = kr * (NCOL * 2) + (((nc >> 3) ^ swz_w<BCR>(kr)) << 4) + ((nc & 7) << 1);
-          const int b1 = (kr + 4) * (NCOL * 2) + (((nc >> 3) ^ swz_w<BCR>(kr + 4)) << 4) + ((nc & 7) << 1);
-          const shortx4 wlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sw + b0));
-          const shortx4 whi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sw + b1));
-          float wv[8];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            wv[u] = bf16_to_f32((uint16_t)wlo[u]);
-            wv[u + 4] = bf16_to_f32((uint16_t)whi[u]);
+          for (int h = 0; h < 2; ++h) {
+            *reinterpret_cast<float4*>(blk + 4 * h) = float4{bf16_lo(xw[2 * h]), bf16_hi(xw[2 * h]),
+                                                             bf16_lo(xw[2 * h + 1]), bf16_hi(xw[2 * h + 1])};
+            *reinterpret_cast<float4*>(blk + d + 4 * h) = float4{bf16_to_f32(wg[4 * h]), bf16_to_f32(wg[4 * h + 1]),
+                                                                 bf16_to_f32(wg[4 * h + 2]), bf16_to_f32(wg[4 * h + 3])};
+            if constexpr (NOISY)
+              *reinterpret_cast<float4*>(blk + 2 * d + 4 * h) = float4{bf16_to_f32(wn[4 * h]), bf16_to_f32(wn[4 * h + 1]),
+                                                                       bf16_to_f32(wn[4 * h + 2]), bf16_to_f32(wn[4 * h + 3])};
           }
-          uint4 xv[NF];
-#pragma unroll
-          for (int q = 0; q < NF; ++q) xv[q] = sx[(f0 * NF + q) * F_CPR + q8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int q = 0; q < NF; ++q) {
-              const uint32_t w2 = (&xv[q].x)[u >> 1];
-              const float xs = (u & 1) ? bf16_hi(w2) : bf16_lo(w2);
-              accv[q] = __builtin_fmaf(xs, wv[u], accv[q]);
-            }
         };
-        if (!busy) {
-          // token slot past the flagged tokens: loads and barriers only
-        } else if (nj == F_BK) {
-#pragma unroll
-          for (int q8 = 0; q8 < F_CPR; ++q8) do_q8(q8);  // full stage: every LDS read can be issued early
-        } else {
-          for (int q8 = 0; q8 < nj / 8; ++q8) do_q8(q8);
+        const int nit = pr * n8;
+        for (int it = tid; it < nit; it += 1024) {  // two items per pass, their loads in flight together
+          gather(it);
+          if (it + 512 < nit) gather(it + 512);
         }
-      }
-      block_barrier();  // the ring is reused by the next round
-#pragma unroll
-      for (int q = 0; q < NF; ++q) {
-        const int fi = base + f0 * NF + q;
-        const bool on = fi < nflag;
-        const int m = flist_s[min(fi, nflag - 1)];
-        const int64_t t = t0 + m;
-        if constexpr (NOISY) {
-          const float accn = __shfl_xor(accv[q], 32);  // column c + 32 holds the same expert's noise logit
-          const int e = 32 * (c >> 6) + (c & 31);
-          if (on && !(c & 32) && e < E) {
-            float cl = accv[q];
-            if (a.bias) cl = cl + a.bias[e];
+        __syncthreads();
+        if (tid < pr) {
+          const int m = pair_tok[p0 + tid], e = pair_e[p0 + tid];
+          const int64_t t = t0 + m;
+          const float4* bx = reinterpret_cast<const float4*>(smem + OFF_ST + tid * pb);
+          const float4* bw = bx + d / 4;
+          const float4* bn = bx + d / 2;
+          float acc = 0.0f, accn = 0.0f;
+#pragma unroll 8
+          for (int j4 = 0; j4 < d / 4; ++j4) {
+            const float4 xv = bx[j4], wv = bw[j4];
+            acc = __builtin_fmaf(xv.x, wv.x, acc);
+            acc = __builtin_fmaf(xv.y, wv.y, acc);
+            acc = __builtin_fmaf(xv.z, wv.z, acc);
+            acc = __builtin_fmaf(xv.w, wv.w, acc);
+            if constexpr (NOISY) {
+              const float4 nv = bn[j4];
+              accn = __builtin_fmaf(xv.x, nv.x, accn);
+              accn = __builtin_fmaf(xv.y, nv.y, accn);
+              accn = __builtin_fmaf(xv.z, nv.z, accn);
+              accn = __builtin_fmaf(xv.w, nv.w, accn);
+            }
+          }
+          float cl = acc;
+          if (a.bias) cl = cl + a.bias[e];
+          if constexpr (NOISY) {
             const float sp = canon_softplus(accn);
-            const float h = __builtin_fmaf(a.noise[t * E + e], sp, cl);
-            Hs[m * HS + e] = h;
+            Hs[m * HS + e] = __builtin_fmaf(a.noise[t * E + e], sp, cl);
             a.CL[t * a.lpad + e] = cl;
             a.SG[t * a.lpad + e] = sp;
-          }
-        } else {
-          const int e = c;
-          if (on && e < E) {
-            float cl = accv[q];
-            if (a.bias) cl = cl + a.bias[e];
+          } else {
             Hs[m * HS + e] = cl;
           }
         }
+        __syncthreads();  // the staging area is refilled by the next round
       }
-      return RT;
-    };
-    for (int base = 0; base < nflag;) {
-      const int need = (nflag - base + TPR - 1) / TPR;  // tokens per thread still needed
-      if (need <= 1) base += round(base, std::integral_constant<int, 1>{});
-      else if (need <= 2 || NFG < 4) base += round(base, std::integral_constant<int, (NFG < 2 ? NFG : 2)>{});
-      else if (need <= 4 || NFG < 8) base += round(base, std::integral_constant<int, (NFG < 4 ? NFG : 4)>{});
-      else if (need <= 8 || NFG < 16) base += round(base, std::integral_constant<int, (NFG < 8 ? NFG : 8)>{});
-      else base += round(base, std::integral_constant<int, NFG>{});
+    } else {
+      constexpr int TPR = 512 / NCOL;  // token slots
+      constexpr int NFG = FR / TPR;    // tokens per thread
+      const int f0 = tid / NCOL, c = tid % NCOL;
+      const int32x4 rsXall = buffer_rsrc(a.x, (uint32_t)(T * d * 2));
+      const uint32_t fl0 = lds_address(&smem_u4[OFF_CV / 16]);
+      uint32_t fvoff[F_NR];  // byte offsets (x offsets can pass 2^31; T*d*2 < 2^32 is checked on the host)
+      bool fisW[F_NR], fact[F_NR];
+      int fld = 0;
+#pragma unroll
+      for (int i = 0; i < F_NR; ++i) {
+        fact[i] = (i * 512 + wave * 64) < F_CH;  // wave-uniform (the x chunks may fill part of a wave)
+        fisW[i] = (i * 512 + wave * 64) < F_WCH;
+        fld += fact[i] ? 1 : 0;
+        const int cc = tid + 512 * i;
+        const int kr = cc / BCR, p = cc % BCR;
+        fvoff[i] = (uint32_t)(kr * NCOL * 2 + ((p ^ swz_w<BCR>(kr)) << 4));  // weight chunks (x chunks set per round)
+      }
+      // One round: NF tokens per thread (TPR * NF tokens), chains interleaved over
+      // the tokens so consecutive fmas are independent.
+      auto round = [&](int base, auto nf_tag) {
+        constexpr int NF = decltype(nf_tag)::value;
+        constexpr int RT = TPR * NF;  // tokens in this round
+        // x chunk slots: row r of the round (token flist[base + r], or a valid row), chunk p
+#pragma unroll
+        for (int i = 0; i < F_NR; ++i) {
+          const int cc = tid + 512 * i - F_WCH;
+          if (cc >= 0) {
+            const int r = min(cc / F_CPR, FR - 1), p = cc % F_CPR;  // lanes past the x chunks: any valid offset
+            const int m = flist_s[min(base + r, nflag - 1)];
+            fvoff[i] = (uint32_t)((t0 + m) * d * 2) + (uint32_t)(p << 4);
+          }
+        }
+        auto fissue = [&](int kt) {
+          const int st = kt % F_STAGES;
+#pragma unroll
+          for (int i = 0; i < F_NR; ++i) {
+            if (!fact[i]) continue;
+            const uint32_t dst = fl0 + (uint32_t)((st * F_CH + i * 512 + wave * 64) * 16);
+            if (fisW[i]) {
+              load_to_lds(__builtin_amdgcn_readfirstlane(dst), (int)(fvoff[i] + (uint32_t)(kt * F_BK * NCOL * 2)), rsW, 0);
+            } else if (tid + 512 * i < F_CH) {  // x chunks: every slot loads (slots past this round's rows repeat a
+                                                 // valid row), so every wave with fact[i] issues the load its waits count
+              load_to_lds(__builtin_amdgcn_readfirstlane(dst), (int)(fvoff[i] + (uint32_t)(kt * F_BK * 2)), rsXall, 0);
+            }
+          }
+        };
+        float accv[NF];
+#pragma unroll
+        for (int q = 0; q < NF; ++q) accv[q] = 0.0f;
+        const bool busy = base + f0 * NF < nflag;  // wave-uniform (a wave's columns share one token slot)
+        const int fnk = (d + F_BK - 1) / F_BK;
+#pragma unroll
+        for (int t = 0; t < F_STAGES - 1; ++t)
+          if (t < fnk) fissue(t);
+        for (int kt = 0; kt < fnk; ++kt) {
+          wait_stages<F_STAGES - 2>(fld, min(F_STAGES - 2, fnk - 1 - kt));
+          block_barrier();  // stage kt in LDS for every wave; the buffer of stage kt-1 is free
+          if (kt + F_STAGES - 1 < fnk) fissue(kt + F_STAGES - 1);
+          const char* sb = smem + OFF_CV + (kt % F_STAGES) * F_CH * 16;
+          lds_char* sw = (lds_char*)(&smem_u4[OFF_CV / 16 + (kt % F_STAGES) * F_CH]);
+          const uint4* sx = reinterpret_cast<const uint4*>(sb + F_WCH * 16);
+          const int nj = min(F_BK, d - kt * F_BK);  // a multiple of 8
+          auto do_q8 = [&](int q8) {
+            // column c's weights of rows 8 q8 .. +7 by two transposing reads: the lanes
+            // of a 16-lane group hold 16 consecutive columns, source lane s points at
+            // row 8 q8 + s/4, columns 4 (s%4) .. +3 of the group
+            const int kr = q8 * 8 + ((lane & 15) >> 2);
+            const int nc = (c - lane) + 16 * (lane >> 4) + 4 * (lane & 3);
+            const int b0 = kr * (NCOL * 2) + (((nc >> 3) ^ swz_w<BCR>(kr)) << 4) + ((nc & 7) << 1);
+            const int b1 = (kr + 4) * (NCOL * 2) + (((nc >> 3) ^ swz_w<BCR>(kr + 4)) << 4) + ((nc & 7) << 1);
+            const shortx4 wlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sw + b0));
+            const shortx4 whi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sw + b1));
+            float wv[8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              wv[u] = bf16_to_f32((uint16_t)wlo[u]);
+              wv[u + 4] = bf16_to_f32((uint16_t)whi[u]);
+            }
+            uint4 xv[NF];
+#pragma unroll
+            for (int q = 0; q < NF; ++q) xv[q] = sx[(f0 * NF + q) * F_CPR + q8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+              for (int q = 0; q < NF; ++q) {
+                const uint32_t w2 = (&xv[q].x)[u >> 1];
+                const float xs = (u & 1) ? bf16_hi(w2) : bf16_lo(w2);
+                accv[q] = __builtin_fmaf(xs, wv[u], accv[q]);
+              }
+          };
+          if (!busy) {
+            // token slot past the flagged tokens: loads and barriers only
+          } else if (nj == F_BK) {
+#pragma unroll
+            for (int q8 = 0; q8 < F_CPR; ++q8) do_q8(q8);  // full stage: every LDS read can be issued early
+          } else {
+            for (int q8 = 0; q8 < nj / 8; ++q8) do_q8(q8);
+          }
+        }
+        block_barrier();  // the ring is reused by the next round
+#pragma unroll
+        for (int q = 0; q < NF; ++q) {
+          const int fi = base + f0 * NF + q;
+          const bool on = fi < nflag;
+          const int m = flist_s[min(fi, nflag - 1)];
+          const int64_t t = t0 + m;
+          if constexpr (NOISY) {
+            const float accn = __shfl_xor(accv[q], 32);  // column c + 32 holds the same expert's noise logit
+            const int e = 32 * (c >> 6) + (c & 31);
+            if (on && !(c & 32) && e < E) {
+              float cl = accv[q];
+              if (a.bias) cl = cl + a.bias[e];
+              const float sp = canon_softplus(accn);
+              const float h = __builtin_fmaf(a.noise[t * E + e], sp, cl);
+              Hs[m * HS + e] = h;
+              a.CL[t * a.lpad + e] = cl;
+              a.SG[t * a.lpad + e] = sp;
+            }
+          } else {
+            const int e = c;
+            if (on && e < E) {
+              float cl = accv[q];
+              if (a.bias) cl = cl + a.bias[e];
+              Hs[m * HS + e] = cl;
+            }
+          }
+        }
+        return RT;
+      };
+      for (int base = 0; base < nflag;) {
+        const int need = (nflag - base + TPR - 1) / TPR;  // tokens per thread still needed
+        if (need <= 1) base += round(base, std::integral_constant<int, 1>{});
+        else if (need <= 2 || NFG < 4) base += round(base, std::integral_constant<int, (NFG < 2 ? NFG : 2)>{});
+        else if (need <= 4 || NFG < 8) base += round(base, std::integral_constant<int, (NFG < 4 ? NFG : 4)>{});
+        else if (need <= 8 || NFG < 16) base += round(base, std::integral_constant<int, (NFG < 8 ? NFG : 8)>{});
+        else base += round(base, std::integral_constant<int, NFG>{});
+      }
     }
     __syncthreads();
     for (int q = wave; q < nflag; q += 8) reselect(flist_s[q]);
