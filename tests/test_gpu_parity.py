@@ -330,6 +330,31 @@ def test_zero_gate_ties_and_identity_experts(moelib, dev):
     assert np.all(y[C:] == 0.0)
 
 
+@pytest.mark.parametrize("name,over", [("switch_top1", dict(T=2048)), ("gshard_top2", dict(T=1024))])
+def test_twin_gate_columns(moelib, dev, name, over):
+    """Every gate column has an identical twin (column 2j+1 = column 2j), so every
+    token's top-(k+1) ties exactly: no token is certified, and each block
+    recomputes the tied candidates of all its tokens canonically (over a hundred
+    (token, expert) pairs, several LDS rounds). Ties go to the lower expert index."""
+    from sparsely_gated_mixture_gate_amd.buffers import to_device
+
+    cfg = scaled(CONFIGS[name], **over)
+    inp = make_inputs(cfg)
+    wg = inp["w_gate"].copy()
+    wg[:, 1::2] = wg[:, 0::2]
+    inp["w_gate"] = wg
+    spec = oracle.LayerSpec.of(cfg, capacity=-1)
+    r = oracle.route(spec, inp)
+    C = oracle.capacity(cfg.T, cfg.E, cfg.k, cfg.capacity_factor, -1)
+    c = dict(cfg=cfg, spec=spec, inp=inp, route=r, C=C, disp=oracle.dispatch(r["topk_idx"], cfg.E, C),
+             dev={k_: to_device(v) for k_, v in inp.items()}, cap=-1)
+    assert np.all(r["topk_idx"][:, 0] % 2 == 0)  # the oracle breaks the ties toward the lower index
+    say(f"[forward-twin-columns] {cfg.name}")
+    fb = _run_forward(moelib, c, dev)
+    rng = np.random.default_rng(5)
+    _check_forward(c, fb, np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 48)])))
+
+
 def test_forward_is_deterministic(moelib, dev):
     from sparsely_gated_mixture_gate_amd.buffers import to_numpy
 
