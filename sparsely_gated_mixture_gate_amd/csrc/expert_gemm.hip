@@ -563,7 +563,10 @@ hipError_t launch_ffn_act(const FfnLaunch& a, hipStream_t s) {
     case kTiles160Skip: return launch_bf16<160, 32, 4, ACT, true, false, 8, 96, 384, 32, 3, 512, 128>(a, s);
     case kTiles256Skip: return launch_bf16<256, 32, 4, ACT, true, true>(a, s);
     case kTiles256: return launch_bf16<256, 32, 4, ACT, false, true>(a, s);
-    default: return launch_bf16<128, 32, 3, ACT, false, false, 8, 128, 512, 32, 3, 512, 128>(a, s);
+    // about one M-tile of rows per expert, no capacity: 256-column tiles on both layers
+    // (twice the tiles of 512-column ones, so the tile rounds of a skewed routing stay
+    // fuller: layer 2 of noisy_top4 has ~320 M-tiles for 256 CUs)
+    default: return launch_bf16<128, 32, 3, ACT, false, false, 8, 64, 256>(a, s);
   }
 }
 
