@@ -131,9 +131,10 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
 // SCAN = false: blk_base holds the exclusive prefixes of the block counts along
 // each expert and offsets the segment starts (written by the scan kernel).
 // SCAN = true (small count tables): blk_base holds the raw block counts; every
-// block derives its own prefixes and the offsets from them, and block 0 also
-// writes counts_kept, offsets, the FFN tile map and the losses (as the scan
-// kernel would), so no separate scan launch is needed.
+// rank block derives its own prefixes and the offsets from them, and one extra
+// block (blockIdx.x == nb, no ranks) writes counts_kept, offsets, the FFN tile
+// map and the losses (as the scan kernel would), so no separate scan launch is
+// needed and that work runs beside the ranks instead of before block 0's.
 template <bool SCAN>
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __restrict__ idx, int64_t n, int k,
                                                             int E, int nbits, int nb, int64_t C,
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
     }
     if (threadIdx.x == 255) off_s[E] = (int)incl;
     __syncthreads();
-    if (blockIdx.x == 0) {
+    if (blockIdx.x == nb) {  // the extra block: offsets, kept counts, tile map and losses, no ranks
       for (int e = threadIdx.x; e <= E; e += 256) so.offsets[e] = off_s[e];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -219,6 +220,7 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
       }
       if (so.route_tail && so.aux_out)
         tail::aux_block<256>(so.counts_routed, so.red, E, so.T, so.k, so.noisy, so.aux_out, sh);
+      return;
     }
   }
   __syncthreads();
@@ -321,7 +323,8 @@ hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s) {
   while ((1 << nbits) < a.E) ++nbits;
   const int y_chunks = a.d * (a.dtype == 1 ? 2 : 4) / 16;
   if (scan_in_rank) {
-    hipLaunchKernelGGL(dispatch_rank_kernel<true>, dim3(nb), dim3(256), sizeof(int) * (6 * a.E + 1), s, a.topk_idx,
+    // nb rank blocks and one block for offsets, tile map and losses, which then run side by side
+    hipLaunchKernelGGL(dispatch_rank_kernel<true>, dim3(nb + 1), dim3(256), sizeof(int) * (6 * a.E + 1), s, a.topk_idx,
                        n, a.k, a.E, nbits, nb, a.C, a.blk_cnt, a.offsets, a.slot_dest, a.row_src,
                        static_cast<uint4*>(a.y_zero), y_chunks, a);
   } else {
