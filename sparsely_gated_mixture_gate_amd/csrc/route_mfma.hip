@@ -443,6 +443,73 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     wsum[wave * 64 + lane] = s_w;
   };
 
+  // phase 1 for blocks of at most 32 tokens: lane = (token lane % 32, half lane / 32)
+  // of this wave's experts, so all 64 lanes scan; each lane then inserts the other
+  // half's sorted top-KK (the top-KK under value desc, index asc is the same in any
+  // insertion order) and the two partial softmax sums are rescaled to the wave max.
+  auto scan_halves = [&]() {
+    constexpr int EH = EPW / 2;
+    const int tl = lane & 31, h = lane >> 5;
+    const int w_lo = min(E, wave * EPW), w_hi = min(E, w_lo + EPW);
+    const int e_lo = min(w_hi, w_lo + h * EH), e_hi = min(w_hi, e_lo + EH);
+    const float* hrow = Hs + tl * HS;
+    float bv[KK];
+    int bi[KK];
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
+      bv[r] = -INFINITY;
+      bi[r] = 0x7FFFFFFF;
+    }
+    auto insert = [&](float v, int i) {
+      if (!better(v, i, bv[KK - 1], bi[KK - 1])) return;
+#pragma unroll
+      for (int r = 0; r < KK; ++r) {
+        if (better(v, i, bv[r], bi[r])) {
+          const float tv = bv[r];
+          const int ti = bi[r];
+          bv[r] = v;
+          bi[r] = i;
+          v = tv;
+          i = ti;
+        }
+      }
+    };
+    float hv[EH];
+#pragma unroll
+    for (int c = 0; c < EH; ++c) hv[c] = e_lo + c < e_hi ? hrow[e_lo + c] : -INFINITY;
+#pragma unroll
+    for (int c = 0; c < EH; ++c)
+      if (e_lo + c < e_hi) insert(hv[c], e_lo + c);
+    const float m_h = bv[0];
+    float s_h = 0.0f;
+#pragma unroll
+    for (int c = 0; c < EH; ++c)
+      if (e_lo + c < e_hi) s_h += fast_exp(hv[c] - m_h);
+    const bool have_h = e_lo < e_hi;
+    const bool have_o = __shfl_xor((int)have_h, 32) != 0;
+    const float m_o = __shfl_xor(m_h, 32), s_o = __shfl_xor(s_h, 32);
+    float ov[KK];
+    int oi[KK];
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
+      ov[r] = __shfl_xor(bv[r], 32);
+      oi[r] = __shfl_xor(bi[r], 32);
+    }
+#pragma unroll
+    for (int r = 0; r < KK; ++r)
+      if (oi[r] != 0x7FFFFFFF) insert(ov[r], oi[r]);
+    const float m_w = bv[0];
+    const float s_w = (have_h ? s_h * fast_exp(m_h - m_w) : 0.0f) + (have_o ? s_o * fast_exp(m_o - m_w) : 0.0f);
+    // every lane writes its token's lists (lanes 32..63 into slots no token uses)
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
+      cand_v[(wave * KK + r) * 64 + lane] = bv[r];
+      cand_i[(wave * KK + r) * 64 + lane] = bi[r];
+    }
+    wmax[wave * 64 + lane] = w_lo < w_hi ? m_w : -INFINITY;
+    wsum[wave * 64 + lane] = s_w;
+  };
+
   // phase 2 (wave 0), lane = token: merge the 8 sorted lists, softmax, gates;
   // certify = check the gaps (first pass) or accept (canonical logits)
   // token tl's results from its top-KK values / indices (value desc, index asc),
@@ -587,7 +654,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   };
 
 
-  scan();
+  if (a.tpb <= 32) scan_halves();
+  else scan();
   __syncthreads();
   if (wave == 0) {
     const bool ok = merge();
