@@ -119,14 +119,18 @@ moe_status moe_workspace_size(const moe_params* p, int op, size_t* bytes);
  * 0: full-softmax probability.
  * Certified MFMA gate (gate_mode AUTO, bf16, E <= 256, logits_out NULL): the
  * logits are computed with bf16 MFMAs (exact products, fp32 sums in the
- * hardware's order) together with sum_j |x[t,j] w[j,e]|, which bounds the
- * distance B to the canonical value (4 d 2^-24 sum|x w| plus the rounding of the
- * bias add, softplus and fma). A token whose k gaps between consecutive values
- * of its top-(k+1) all exceed twice its largest B has the canonical routing;
- * every other token is recomputed with the canonical chains. topk_idx and
- * counts_routed are therefore those of the canonical logits in every mode; the
- * gates, aux losses and load estimates of certified tokens use the MFMA logits
- * (rounding-level differences).
+ * hardware's order) together with S = sum_j |x[t,j] w[j,e]| and Q = the sum of
+ * |accumulator| over the M = ceil(d/32) k-steps, which bound the distance to the
+ * canonical value by B = 100 2^-24 (Q + S)(1 + 256 2^-24 M) (plus the rounding of
+ * the bias add, softplus and fma). A token whose k gaps between consecutive
+ * values of its top-(k+1) all exceed twice its largest B has the canonical
+ * routing. For every other token, the experts whose MFMA value lies within 2B
+ * of its (k+1)-th value (the only ones that can be in the canonical top-(k+1))
+ * get their logits recomputed with the canonical chains, or the whole row is
+ * recomputed where those do not fit, and the token is selected again. topk_idx
+ * and counts_routed are therefore those of the canonical logits in every mode;
+ * the gates, aux losses and load estimates use the MFMA logits where they were
+ * not recomputed (rounding-level differences).
  * Inputs:  x [T,d] dtype; w_gate [d,E] dtype; gate_bias [E] fp32 or NULL;
  *          w_noise [d,E] dtype or NULL; noise [T,E] fp32 standard normals
  *          (required iff w_noise).
