@@ -25,11 +25,13 @@
 // the fma with eps add their own rounding terms. If, for the top-(k+1) MFMA
 // values v_1 >= ..., every gap v_r - v_{r+1} (r = 1..k) exceeds twice the
 // token's largest B, the canonical values keep the same order and the same
-// top-k set, so the token's routing is the canonical one. Other tokens (and
-// every token when the caller asks for it) recompute their logits with the
-// canonical chains inside the block and are selected again. Gate values of
-// certified tokens use the MFMA logits (their deviation from the canonical-logit
-// gates is a rounding-level effect, far inside the bf16 output tolerance).
+// top-k set, so the token's routing is the canonical one. Other tokens
+// recompute, with the canonical chains inside the block, the logits of the
+// experts that can still be in the canonical top-(k+1) (MFMA value within 2B of
+// the (k+1)-th), or their whole rows (always when the caller asks for the
+// fallback), and are selected again. Gate values use the MFMA logits where they
+// were not recomputed (their deviation from the canonical-logit gates is a
+// rounding-level effect, far inside the bf16 output tolerance).
 //
 // One block = 64 tokens, 512 threads (8 waves):
 //   GEMM: x tile [64][32] and weight tile [32][NCOL] per stage in an LDS ring
