@@ -4,7 +4,9 @@ Thin ctypes marshalling over the C ABI in ``include/moe.h``: each function
 here has the name of the C entry point it calls, takes torch tensors (device
 memory) and passes their pointers and the current HIP stream. Every step of
 the layer runs in the library's HIP kernels; nothing here computes. If the
-library is missing, importing this package raises -- there is no fallback.
+library is missing, the first call raises -- there is no fallback. The
+library is loaded on first use, not at import, so the package (and its build
+module) can be imported before anything is built.
 
 Build the library with ``python -m sparsely_gated_mixture_gate_amd.build`` or
 ``__graft_entry__.build()``.
@@ -51,6 +53,9 @@ class moe_params(ctypes.Structure):
     ]
 
 
+_LIB = None
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
@@ -83,7 +88,12 @@ def _load():
     return lib
 
 
-_lib = _load()
+def lib() -> ctypes.CDLL:
+    """The loaded ``libmoe.so`` (loaded on the first call; raises if it is not built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
 
 
 # --------------------------------------------------------------------------
@@ -107,7 +117,7 @@ def _stream(stream):
 
 def _check(st: int, where: str):
     if st != MOE_OK:
-        raise MoEError(st, where, _lib.moe_last_error().decode())
+        raise MoEError(st, where, lib().moe_last_error().decode())
 
 
 def _ws(ws):
@@ -117,7 +127,7 @@ def _ws(ws):
 
 
 def status_string(status: int) -> str:
-    return _lib.moe_status_string(status).decode()
+    return lib().moe_status_string(status).decode()
 
 
 def make_params(T, d_model, d_ff, E, k, dtype="bf16", act="gelu", renormalize=False, capacity_factor=0.0,
@@ -129,16 +139,16 @@ def make_params(T, d_model, d_ff, E, k, dtype="bf16", act="gelu", renormalize=Fa
 
 
 def moe_capacity(p: moe_params) -> int:
-    return int(_lib.moe_capacity(ctypes.byref(p)))
+    return int(lib().moe_capacity(ctypes.byref(p)))
 
 
 def moe_max_rows(p: moe_params) -> int:
-    return int(_lib.moe_max_rows(ctypes.byref(p)))
+    return int(lib().moe_max_rows(ctypes.byref(p)))
 
 
 def moe_workspace_size(p: moe_params, op: int) -> int:
     n = ctypes.c_size_t(0)
-    _check(_lib.moe_workspace_size(ctypes.byref(p), int(op), ctypes.byref(n)), "moe_workspace_size")
+    _check(lib().moe_workspace_size(ctypes.byref(p), int(op), ctypes.byref(n)), "moe_workspace_size")
     return int(n.value)
 
 
@@ -148,37 +158,37 @@ def moe_workspace_size(p: moe_params, op: int) -> int:
 def moe_route(p, x, w_gate, gate_bias, w_noise, noise, topk_idx, topk_gate, counts_routed, aux_out=None,
               logits_out=None, ws=None, stream=None):
     wp, wn = _ws(ws)
-    _check(_lib.moe_route(ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(gate_bias), _ptr(w_noise), _ptr(noise),
+    _check(lib().moe_route(ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(gate_bias), _ptr(w_noise), _ptr(noise),
                           _ptr(topk_idx), _ptr(topk_gate), _ptr(counts_routed), _ptr(aux_out), _ptr(logits_out),
                           wp, wn, _stream(stream)), "moe_route")
 
 
 def moe_dispatch(p, x, topk_idx, counts_kept, offsets, slot_dest, row_src, x_perm, ws=None, stream=None):
     wp, wn = _ws(ws)
-    _check(_lib.moe_dispatch(ctypes.byref(p), _ptr(x), _ptr(topk_idx), _ptr(counts_kept), _ptr(offsets),
+    _check(lib().moe_dispatch(ctypes.byref(p), _ptr(x), _ptr(topk_idx), _ptr(counts_kept), _ptr(offsets),
                              _ptr(slot_dest), _ptr(row_src), _ptr(x_perm), wp, wn, _stream(stream)), "moe_dispatch")
 
 
 def moe_expert_ffn(p, x_perm, offsets, w1, w2, y_perm, ws=None, stream=None):
     wp, wn = _ws(ws)
-    _check(_lib.moe_expert_ffn(ctypes.byref(p), _ptr(x_perm), _ptr(offsets), _ptr(w1), _ptr(w2), _ptr(y_perm),
+    _check(lib().moe_expert_ffn(ctypes.byref(p), _ptr(x_perm), _ptr(offsets), _ptr(w1), _ptr(w2), _ptr(y_perm),
                                wp, wn, _stream(stream)), "moe_expert_ffn")
 
 
 def moe_combine(p, y_perm, slot_dest, topk_gate, y, stream=None):
-    _check(_lib.moe_combine(ctypes.byref(p), _ptr(y_perm), _ptr(slot_dest), _ptr(topk_gate), _ptr(y),
+    _check(lib().moe_combine(ctypes.byref(p), _ptr(y_perm), _ptr(slot_dest), _ptr(topk_gate), _ptr(y),
                             _stream(stream)), "moe_combine")
 
 
 def moe_forward(p, x, w_gate, gate_bias, w_noise, noise, w1, w2, y, aux_out=None, topk_idx=None, topk_gate=None,
                 counts_routed=None, counts_kept=None, slot_dest=None, ws=None, stream=None):
     wp, wn = _ws(ws)
-    _check(_lib.moe_forward(ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(gate_bias), _ptr(w_noise), _ptr(noise),
+    _check(lib().moe_forward(ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(gate_bias), _ptr(w_noise), _ptr(noise),
                             _ptr(w1), _ptr(w2), _ptr(y), _ptr(aux_out), _ptr(topk_idx), _ptr(topk_gate),
                             _ptr(counts_routed), _ptr(counts_kept), _ptr(slot_dest), wp, wn, _stream(stream)),
            "moe_forward")
 
 
 def moe_canonical_softplus(z, out, stream=None):
-    _check(_lib.moe_canonical_softplus(_ptr(z), _ptr(out), int(z.numel()), _stream(stream)),
+    _check(lib().moe_canonical_softplus(_ptr(z), _ptr(out), int(z.numel()), _stream(stream)),
            "moe_canonical_softplus")

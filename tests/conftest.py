@@ -29,4 +29,5 @@ def moelib():
         _b.build()
     import sparsely_gated_mixture_gate_amd as m
 
+    m.lib()  # fails here, loudly, if the library cannot be loaded
     return m
