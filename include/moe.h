@@ -18,7 +18,8 @@
  *   - Every pointer argument is a DEVICE pointer to contiguous row-major data,
  *     aligned to 16 bytes, owned by the caller, unless stated otherwise. The
  *     library allocates no device memory and keeps no state between calls
- *     except a thread-local error string.
+ *     except a thread-local error string and the thread-local phase events of
+ *     moe_set_phase_events.
  *   - "dtype" tensors (x, w_gate, w_noise, w1, w2, x_perm, y_perm, y) are all
  *     bf16 (raw 16-bit patterns) or all fp32, per moe_params.dtype. Logits,
  *     gates, noise, gate_bias and aux are always fp32; indices are int32.
@@ -206,6 +207,21 @@ moe_status moe_forward(const moe_params* p, const void* x, const void* w_gate, c
                        const void* w_noise, const float* noise, const void* w1, const void* w2, void* y,
                        float* aux_out, int32_t* topk_idx, float* topk_gate, int32_t* counts_routed,
                        int32_t* counts_kept, int32_t* slot_dest, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_set_phase_events -- phase timing of moe_forward (a measurement aid; the
+ * layer's results do not depend on it).
+ * After this call, every moe_forward on the calling thread records events[i]
+ * (hipEvent_t handles, created by the caller) on its stream at these points:
+ *   0 before the route, 1 after the route, 2 after the dispatch, 3 after the
+ *   first expert layer's launch, 4 after the second expert layer's launch,
+ *   5 at the end (after the combine; top-1 bf16 layers have none).
+ * Entries i >= n, or NULL, are not recorded. n = 0 or events = NULL turns the
+ * recording off. The library keeps the handles, not copies: the events must
+ * outlive the calls that record them. Thread-local.
+ * Returns MOE_ERR_INVALID_ARG unless 0 <= n <= 6.
+ */
+moe_status moe_set_phase_events(void* const* events, int n);
 
 /*
  * moe_canonical_softplus -- the softplus of the noisy gate (Shazeer "Methode",

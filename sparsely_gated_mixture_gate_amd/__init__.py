@@ -28,6 +28,7 @@ MOE_GATE_AUTO, MOE_GATE_CANONICAL, MOE_GATE_FALLBACK = range(3)
 EXPORTED = (
     "moe_status_string", "moe_last_error", "moe_capacity", "moe_max_rows", "moe_workspace_size",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_canonical_softplus",
+    "moe_set_phase_events",
 )
 
 
@@ -80,6 +81,7 @@ def _load():
         "moe_combine": ([PP, P, P, P, P, P], i32),
         "moe_forward": ([PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
         "moe_canonical_softplus": ([P, P, i64, P], i32),
+        "moe_set_phase_events": ([ctypes.POINTER(P), i32], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -192,3 +194,22 @@ def moe_forward(p, x, w_gate, gate_bias, w_noise, noise, w1, w2, y, aux_out=None
 def moe_canonical_softplus(z, out, stream=None):
     _check(lib().moe_canonical_softplus(_ptr(z), _ptr(out), int(z.numel()), _stream(stream)),
            "moe_canonical_softplus")
+
+
+def moe_set_phase_events(events=None):
+    """Record torch.cuda.Event objects at the phase boundaries of later
+    moe_forward calls on this thread (see include/moe.h); None turns it off.
+    The events must outlive those calls."""
+    if not events:
+        _check(lib().moe_set_phase_events(None, 0), "moe_set_phase_events")
+        return
+    handles = []
+    for ev in events:
+        if ev is None:
+            handles.append(None)
+            continue
+        if not ev.cuda_event:
+            ev.record()  # the runtime creates the event on its first record
+        handles.append(ev.cuda_event)
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    _check(lib().moe_set_phase_events(arr, len(handles)), "moe_set_phase_events")

@@ -154,6 +154,7 @@ struct FfnLaunch {
   int64_t T;
   void* y_out;
   const float* gate;
+  void* mid_event;  // hipEvent_t recorded between the two layers' launches (phase timing), or null
 };
 hipError_t launch_expert_ffn(const FfnLaunch& a, hipStream_t s);
 int ffn_tile_rows(int dtype, int64_t capacity, int64_t max_rows, int E);  // M-tile rows the FFN launch uses

@@ -511,6 +511,7 @@ hipError_t launch_bf16(const FfnLaunch& a, hipStream_t s) {
                      static_cast<const uint16_t*>(a.w1), static_cast<uint16_t*>(a.h1), a.offsets, a.tile_start, a.E,
                      a.d, a.f, nt1, a.x_src ? a.row_src : nullptr, a.T, nullptr, nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (a.mid_event && (err = hipEventRecord(static_cast<hipEvent_t>(a.mid_event), s)) != hipSuccess) return err;
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, NSTAGE, ACT, false, SKIP, NW, WNT, PF>), grid_for(mtiles * nt2),
                      dim3(64 * NW), 0, s, static_cast<const uint16_t*>(a.h1), static_cast<const uint16_t*>(a.w2),
                      static_cast<uint16_t*>(a.y_out ? a.y_out : a.y_perm), a.offsets, a.tile_start, a.E, a.f, a.d, nt2,
@@ -532,6 +533,7 @@ hipError_t launch_f32(const FfnLaunch& a, hipStream_t s) {
                      static_cast<const float*>(a.x_perm), static_cast<const float*>(a.w1),
                      static_cast<float*>(a.h1), a.offsets, a.tile_start, a.E, a.d, a.f, nt1);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (a.mid_event && (err = hipEventRecord(static_cast<hipEvent_t>(a.mid_event), s)) != hipSuccess) return err;
   hipLaunchKernelGGL((grouped_gemm_f32_kernel<ACT, false>), dim3((unsigned)(mtiles * nt2)), dim3(256), 0, s,
                      static_cast<const float*>(a.h1), static_cast<const float*>(a.w2),
                      static_cast<float*>(a.y_perm), a.offsets, a.tile_start, a.E, a.f, a.d, nt2);

@@ -17,6 +17,14 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Phase timing of moe_forward (moe_set_phase_events): caller-owned hipEvent_t handles.
+constexpr int kPhaseEvents = 6;
+thread_local void* g_phase_ev[kPhaseEvents] = {};
+
+hipError_t record_phase(int i, hipStream_t s) {
+  return g_phase_ev[i] ? hipEventRecord(static_cast<hipEvent_t>(g_phase_ev[i]), s) : hipSuccess;
+}
+
 moe_status fail(moe_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 moe_status fail(moe_status st, const char* fmt, ...) {
   char buf[512];
@@ -283,7 +291,8 @@ moe_status run_dispatch(const moe_params* p, const void* x, const int32_t* topk_
 // top-1 bf16 layers only): layer 2 writes the gated rows straight into y.
 moe_status run_ffn(const moe_params* p, const void* x_perm, const int32_t* offsets, const void* w1, const void* w2,
                    void* y_perm, const FfnWs& w, bool tile_map_ready, hipStream_t s, const void* x_src = nullptr,
-                   const int32_t* row_src = nullptr, void* y_out = nullptr, const float* gate = nullptr) {
+                   const int32_t* row_src = nullptr, void* y_out = nullptr, const float* gate = nullptr,
+                   void* mid_event = nullptr) {
   FfnLaunch a;
   a.d = p->d_model;
   a.f = p->d_ff;
@@ -305,6 +314,7 @@ moe_status run_ffn(const moe_params* p, const void* x_perm, const int32_t* offse
   a.T = p->T;
   a.y_out = y_out;
   a.gate = gate;
+  a.mid_event = mid_event;
   const hipError_t e = launch_expert_ffn(a, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "expert FFN launch");
 }
@@ -455,10 +465,13 @@ moe_status moe_forward(const moe_params* p, const void* x, const void* w_gate, c
   int32_t* cr = counts_routed ? counts_routed : w.counts_routed;
   int32_t* ck = counts_kept ? counts_kept : w.counts_kept;
   int32_t* sd = slot_dest ? slot_dest : w.slot_dest;
+  hipError_t he;
+  if ((he = record_phase(0, s)) != hipSuccess) return hip_fail(he, "phase event");
   // the route's per-expert sums and losses run inside the dispatch kernels
   if ((st = run_route(p, x, w_gate, gate_bias, w_noise, noise, idx, gate, cr, aux_out, nullptr, w.route, s, true)) !=
       MOE_OK)
     return st;
+  if ((he = record_phase(1, s)) != hipSuccess) return hip_fail(he, "phase event");
   // bf16: the expert GEMM gathers its rows from x (no x_perm copy); top-1 layers also
   // write the gated expert outputs straight into y (no combine pass; the dispatch
   // zeroes the rows of dropped tokens)
@@ -467,11 +480,22 @@ moe_status moe_forward(const moe_params* p, const void* x, const void* w_gate, c
   if ((st = run_dispatch(p, x, idx, ck, w.offsets, sd, w.row_src, w.x_perm, w.blk_cnt, w.ffn.tile_start, fused,
                          direct_y ? y : nullptr, s, &w.route, cr, aux_out, noisy)) != MOE_OK)
     return st;
+  if ((he = record_phase(2, s)) != hipSuccess) return hip_fail(he, "phase event");
   if ((st = run_ffn(p, w.x_perm, w.offsets, w1, w2, w.y_perm, w.ffn, true, s, fused ? x : nullptr,
-                    fused ? w.row_src : nullptr, direct_y ? y : nullptr, direct_y ? gate : nullptr)) != MOE_OK)
+                    fused ? w.row_src : nullptr, direct_y ? y : nullptr, direct_y ? gate : nullptr,
+                    g_phase_ev[3])) != MOE_OK)
     return st;
-  if (direct_y) return MOE_OK;
-  return run_combine(p, w.y_perm, sd, gate, y, s);
+  if ((he = record_phase(4, s)) != hipSuccess) return hip_fail(he, "phase event");
+  if (!direct_y && (st = run_combine(p, w.y_perm, sd, gate, y, s)) != MOE_OK) return st;
+  if ((he = record_phase(5, s)) != hipSuccess) return hip_fail(he, "phase event");
+  return MOE_OK;
+}
+
+// Phase events of moe_forward on the calling thread (n = 0 or events NULL: off).
+moe_status moe_set_phase_events(void* const* events, int n) {
+  if (n < 0 || n > kPhaseEvents) return fail(MOE_ERR_INVALID_ARG, "n = %d outside [0, %d]", n, kPhaseEvents);
+  for (int i = 0; i < kPhaseEvents; ++i) g_phase_ev[i] = (events && i < n) ? events[i] : nullptr;
+  return MOE_OK;
 }
 
 // Canonical softplus of the noisy gate, element-wise (z, out: n fp32 device values).
