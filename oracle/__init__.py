@@ -53,9 +53,11 @@ def _lib():
             "oracle_load": ([i64, i32, i32, P, P, P, P, i32, P], None),
             "oracle_aux": ([i64, i32, i32, P, P, P, P, P], None),
             "oracle_capacity": ([i64, i32, i32, dbl, i64], i64),
-            "oracle_dispatch": ([i64, i32, i32, i64, P, P, P, P, P, P], None),
+            "oracle_dispatch": ([i64, i32, i32, i64, i32, P, P, P, P, P, P], None),
             "oracle_expert_ffn_rows": ([i64, i32, i32, i32, i32, P, P, P, P, P, P], None),
             "oracle_combine": ([i64, P, i32, i32, P, P, P, P, P], None),
+            "oracle_expert_bwd_rows": ([i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P], None),
+            "oracle_gate_bwd": ([i64, i32, i32, i32, P, P, P, P, P, i32, P, P, P, dbl, P, P, P], None),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(lib, name)
@@ -176,7 +178,9 @@ def capacity(T: int, E: int, k: int, capacity_factor: float, explicit: int = -1)
     return int(_lib().oracle_capacity(T, E, k, float(capacity_factor), int(explicit)))
 
 
-def dispatch(topk_idx, E: int, C: int) -> dict:
+def dispatch(topk_idx, E: int, C: int, slot_major: bool = False) -> dict:
+    """Capacity-limited dispatch. slot_major=False: overflow dropped in token order;
+    True: first-choice priority (all first choices ranked before any second choice)."""
     idx = _c(topk_idx, np.int32)
     T, k = idx.shape
     counts_routed = np.empty(E, np.int32)
@@ -184,8 +188,8 @@ def dispatch(topk_idx, E: int, C: int) -> dict:
     offsets = np.empty(E + 1, np.int32)
     slot_dest = np.empty((T, k), np.int32)
     row_src = np.full(max(T * k, 1), -1, np.int32)
-    _lib().oracle_dispatch(T, E, k, int(C), _p(idx), _p(counts_routed), _p(counts_kept), _p(offsets),
-                           _p(slot_dest), _p(row_src))
+    _lib().oracle_dispatch(T, E, k, int(C), int(bool(slot_major)), _p(idx), _p(counts_routed), _p(counts_kept),
+                           _p(offsets), _p(slot_dest), _p(row_src))
     R = int(offsets[E])
     return dict(counts_routed=counts_routed, counts_kept=counts_kept, offsets=offsets,
                 slot_dest=slot_dest, row_src=row_src[:R].copy(), R=R)
@@ -239,11 +243,12 @@ class LayerSpec:
     renormalize: bool
     capacity_factor: float = 0.0
     capacity: int = -1  # explicit per-expert capacity; -1 derives it from the factor
+    slot_major: bool = False  # drop order: False = token order, True = first-choice priority
 
     @classmethod
-    def of(cls, cfg, capacity: int = -1) -> "LayerSpec":
+    def of(cls, cfg, capacity: int = -1, slot_major: bool = False) -> "LayerSpec":
         return cls(cfg.T, cfg.d_model, cfg.d_ff, cfg.E, cfg.k, cfg.dtype, cfg.act, bool(cfg.renormalize),
-                   float(cfg.capacity_factor), int(capacity))
+                   float(cfg.capacity_factor), int(capacity), bool(slot_major))
 
 
 def route(spec: LayerSpec, inp: dict) -> dict:
@@ -271,7 +276,7 @@ def forward(spec: LayerSpec, inp: dict, tokens=None) -> dict:
     ``y`` then holds one row per listed token, in the listed order."""
     r = route(spec, inp)
     C = capacity(spec.T, spec.E, spec.k, spec.capacity_factor, spec.capacity)
-    disp = dispatch(r["topk_idx"], spec.E, C)
+    disp = dispatch(r["topk_idx"], spec.E, C, spec.slot_major)
     T, k = spec.T, spec.k
     if tokens is None:
         tokens = np.arange(T, dtype=np.int32)
@@ -291,3 +296,102 @@ def forward(spec: LayerSpec, inp: dict, tokens=None) -> dict:
     out.update(disp)
     out.update(C=C, tokens=tokens, y=y, yp=yp, yp_slots=rows_slot)
     return out
+
+
+# --------------------------------------------------------------------------
+# backward pass (the pages train the layer: Shazeer et al. summary page,
+# "Fragen" -- gradients flow through the kept gates because the top-k is taken
+# before the softmax; "Kernideen" -- the noise term keeps them smooth)
+# --------------------------------------------------------------------------
+def expert_bwd_rows(x, x_row, expert, w1, w2, dout, act: str, dtype: str):
+    """fp64 expert FFN backward for rows r (expert[r] applied to x[x_row[r]])
+    with upstream gradient dout[r]. Returns (o, dx_rows, dw1, dw2)."""
+    wd = _wdtype(dtype)
+    x, w1, w2 = _c(x, wd), _c(w1, wd), _c(w2, wd)
+    x_row, expert = _c(x_row, np.int32), _c(expert, np.int32)
+    dout = _c(dout, np.float64)
+    n, d = dout.shape
+    E, _, f = w1.shape
+    o = np.zeros((n, d), np.float64)
+    dx_rows = np.zeros((n, d), np.float64)
+    dw1 = np.empty((E, d, f), np.float64)
+    dw2 = np.empty((E, f, d), np.float64)
+    _lib().oracle_expert_bwd_rows(n, d, f, E, _dcode(dtype), RELU if act == "relu" else GELU, _p(x), _p(x_row),
+                                  _p(expert), _p(w1), _p(w2), _p(dout), _p(o), _p(dx_rows), _p(dw1), _p(dw2))
+    return o, dx_rows, dw1, dw2
+
+
+def gate_bwd(H, clean, sigma, noise, order, k: int, renormalize: bool, g, dg, counts_routed, w_switch: float,
+             dload=None):
+    """dL/dclean [T,E] and (noisy) dL/d(x W_noise) [T,E], fp64."""
+    H, clean = _c(H, np.float32), _c(clean, np.float32)
+    sigma, noise = _c(sigma, np.float32), _c(noise, np.float32)
+    order = _c(order, np.int32)
+    g, dg = _c(g, np.float64), _c(dg, np.float64)
+    counts_routed = _c(counts_routed, np.int32)
+    dload = _c(dload, np.float64)
+    T, E = H.shape
+    dclean = np.empty((T, E), np.float64)
+    du = np.empty((T, E), np.float64) if sigma is not None else None
+    _lib().oracle_gate_bwd(T, E, k, int(bool(renormalize)), _p(H), _p(clean), _p(sigma), _p(noise), _p(order),
+                           order.shape[1], _p(g), _p(dg), _p(counts_routed), float(w_switch), _p(dload),
+                           _p(dclean), _p(du))
+    return dclean, du
+
+
+def cv2_grad(v) -> np.ndarray:
+    """d CV(v)^2 / dv for the population CV (Load-Balancing-Losses); 0 for one entry."""
+    v = np.asarray(v, np.float64)
+    E = v.size
+    if E <= 1:
+        return np.zeros_like(v)
+    mu = v.sum() / E
+    var = ((v - mu) ** 2).sum() / E
+    return 2.0 * (v - mu) / (E * mu * mu) - 2.0 * var / (E * mu ** 3)
+
+
+def backward(spec: LayerSpec, inp: dict, dy, loss_weights=(0.0, 0.0, 0.0)) -> dict:
+    """Gradients of L = sum(dy * y) + w_switch * switch_aux + w_importance *
+    CV(Importance)^2 + w_load * CV(Load)^2 with respect to x, W_gate, gate_bias,
+    W_noise, W1 and W2, with the layer's discrete choices (top-k sets, capacity
+    drops) held fixed. fp64 throughout (logits: the forward's canonical fp32)."""
+    w_switch, w_imp, w_load = (float(w) for w in loss_weights)
+    r = route(spec, inp)
+    C = capacity(spec.T, spec.E, spec.k, spec.capacity_factor, spec.capacity)
+    disp = dispatch(r["topk_idx"], spec.E, C, spec.slot_major)
+    T, k, E = spec.T, spec.k, spec.E
+    dy = np.asarray(dy, np.float64)
+    kept = disp["slot_dest"] >= 0
+    tok = np.repeat(np.arange(T, dtype=np.int32), k).reshape(T, k)
+    rows_tok, rows_exp = tok[kept], r["topk_idx"][kept]
+    g = r["topk_gate"]
+    dout = g[kept][:, None] * dy[rows_tok]
+    o, dx_rows, dw1, dw2 = expert_bwd_rows(inp["x"], rows_tok, rows_exp, inp["w1"], inp["w2"], dout, spec.act,
+                                           spec.dtype)
+    # dL/dg: the combine (kept slots only) plus the importance loss (all slots, pre-drop)
+    dg = np.zeros((T, k), np.float64)
+    dg[kept] = np.einsum("rd,rd->r", dy[rows_tok], o)
+    if w_imp:
+        dg += w_imp * cv2_grad(r["importance"])[r["topk_idx"]]
+    noisy = inp.get("w_noise") is not None
+    dload = w_load * cv2_grad(r["load"]) if (noisy and w_load) else None
+    dclean, du = gate_bwd(r["H"], r["clean"], r["sigma"], inp.get("noise"), r["order"], k, spec.renormalize, g, dg,
+                          r["counts_routed"], w_switch, dload)
+    xf = bf16_widen(inp["x"]) if spec.dtype == "bf16" else np.asarray(inp["x"], np.float64)
+    wg = bf16_widen(inp["w_gate"]) if spec.dtype == "bf16" else np.asarray(inp["w_gate"], np.float64)
+    dx = np.zeros((T, spec.d_model), np.float64)
+    np.add.at(dx, rows_tok, dx_rows)
+    dx += dclean @ wg.T
+    out = dict(dx=dx, dw_gate=xf.T @ dclean, dw1=dw1, dw2=dw2, dg=dg, dclean=dclean, o=o, route=r, disp=disp,
+               dgate_bias=dclean.sum(axis=0) if inp.get("gate_bias") is not None else None,
+               dw_noise=None, du=du)
+    if noisy:
+        wn = bf16_widen(inp["w_noise"]) if spec.dtype == "bf16" else np.asarray(inp["w_noise"], np.float64)
+        dx += du @ wn.T
+        out["dw_noise"] = xf.T @ du
+    return out
+
+
+def bf16_widen(a) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact)."""
+    return (np.ascontiguousarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

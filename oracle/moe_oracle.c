@@ -348,16 +348,29 @@ int64_t oracle_capacity(int64_t T, int E, int k, double capacity_factor, int64_t
 /* slot_dest[t,s] = offsets[e] + rank for kept assignments, else -1;         */
 /* row_src[slot] = t. Rows of the permuted batch are therefore sorted by     */
 /* (expert, token). C < 0 means no limit.                                    */
+/* slot_major = 1: first-choice priority (the GShard row of [Tables]: top-2  */
+/* with a capacity; reading: every token's first choice is served before any */
+/* token's second choice). The walk is then slots outer, tokens inner, so    */
+/* ranks -- and rows within an expert -- follow (slot, token) order.         */
 /* ------------------------------------------------------------------------ */
-void oracle_dispatch(int64_t T, int E, int k, int64_t C, const int32_t* topk_idx, int32_t* counts_routed,
-                     int32_t* counts_kept, int32_t* offsets, int32_t* slot_dest, int32_t* row_src) {
+void oracle_dispatch(int64_t T, int E, int k, int64_t C, int slot_major, const int32_t* topk_idx,
+                     int32_t* counts_routed, int32_t* counts_kept, int32_t* offsets, int32_t* slot_dest,
+                     int32_t* row_src) {
   int64_t* fill = (int64_t*)calloc((size_t)E, sizeof(int64_t));
   int64_t* rank = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T * k > 0 ? T * k : 1));
-  for (int64_t t = 0; t < T; ++t)
-    for (int s = 0; s < k; ++s) {
-      int e = topk_idx[t * k + s];
-      rank[t * k + s] = fill[e]++;
-    }
+  if (slot_major) {
+    for (int s = 0; s < k; ++s)
+      for (int64_t t = 0; t < T; ++t) {
+        int e = topk_idx[t * k + s];
+        rank[t * k + s] = fill[e]++;
+      }
+  } else {
+    for (int64_t t = 0; t < T; ++t)
+      for (int s = 0; s < k; ++s) {
+        int e = topk_idx[t * k + s];
+        rank[t * k + s] = fill[e]++;
+      }
+  }
   int64_t acc = 0;
   for (int e = 0; e < E; ++e) {
     counts_routed[e] = (int32_t)fill[e];
@@ -444,5 +457,175 @@ void oracle_combine(int64_t n_tokens, const int32_t* tokens, int d, int k, const
       const double g = gates[t * k + s];
       for (int j = 0; j < d; ++j) o[j] += g * yp[row * d + j];
     }
+  }
+}
+
+/* ======================================================================== */
+/* Backward pass of the layer (the pages are about training: [Shazeer]      */
+/* "Fragen": the top-k is taken before the softmax, so the kept gate values */
+/* keep continuous derivatives and gradients flow back through the gate;    */
+/* "Kernideen": the noise term gives smooth, backpropagatable gradients).   */
+/* The discrete choices (top-k sets, ranks, drops) are constants of the     */
+/* backward; everything else is differentiated exactly, in fp64.            */
+/* ======================================================================== */
+
+#define ORACLE_PI 3.14159265358979323846
+
+/* d act(z) / dz: ReLU -> 1 for z > 0 (0 at z = 0); exact GELU z Phi(z) ->   */
+/* Phi(z) + z phi(z).                                                        */
+static double act_grad(int act, double z) {
+  if (act == OR_RELU) return z > 0.0 ? 1.0 : 0.0;
+  const double phi = exp(-0.5 * z * z) / sqrt(2.0 * ORACLE_PI);
+  return 0.5 * (1.0 + erf(z / sqrt(2.0))) + z * phi;
+}
+
+/* Expert FFN backward, fp64, for n rows (row r: expert expert[r] applied to */
+/* x[x_row[r]]). dout[r] = dL/d(expert output of row r). Writes the expert  */
+/* outputs o[r] (the forward, recomputed) and dx_rows[r] = dL/dx through    */
+/* this row, and accumulates the weight gradients of every expert:          */
+/*   z = x W1[e], h = act(z), o = h W2[e];                                   */
+/*   dh = W2[e] dout, dz = dh * act'(z), dx = W1[e] dz,                      */
+/*   dW2[e] += h^T dout, dW1[e] += x^T dz.                                   */
+/* Experts run in parallel; each expert's rows are taken in row order, so   */
+/* the sums do not depend on the thread count.                              */
+void oracle_expert_bwd_rows(int64_t n, int d, int f, int E, int dtype, int act, const void* x, const int32_t* x_row,
+                            const int32_t* expert, const void* w1, const void* w2, const double* dout, double* o,
+                            double* dx_rows, double* dw1, double* dw2) {
+  memset(dw1, 0, sizeof(double) * (size_t)E * d * f);
+  memset(dw2, 0, sizeof(double) * (size_t)E * f * d);
+#pragma omp parallel
+  {
+    double* xr = (double*)malloc(sizeof(double) * (size_t)d);
+    double* z = (double*)malloc(sizeof(double) * (size_t)f);
+    double* h = (double*)malloc(sizeof(double) * (size_t)f);
+    double* dz = (double*)malloc(sizeof(double) * (size_t)f);
+#pragma omp for schedule(dynamic, 1)
+    for (int e = 0; e < E; ++e) {
+      const int64_t w1b = (int64_t)e * d * f, w2b = (int64_t)e * f * d;
+      for (int64_t r = 0; r < n; ++r) {
+        if (expert[r] != e) continue;
+        const int64_t t = x_row[r];
+        for (int j = 0; j < d; ++j) xr[j] = elem(x, dtype, t * d + j);
+        for (int i = 0; i < f; ++i) z[i] = 0.0;
+        for (int j = 0; j < d; ++j)
+          for (int i = 0; i < f; ++i) z[i] += xr[j] * (double)elem(w1, dtype, w1b + (int64_t)j * f + i);
+        for (int i = 0; i < f; ++i)
+          h[i] = (act == OR_RELU) ? (z[i] > 0.0 ? z[i] : 0.0) : 0.5 * z[i] * (1.0 + erf(z[i] / sqrt(2.0)));
+        const double* go = dout + r * d;
+        double* orow = o + r * d;
+        for (int j = 0; j < d; ++j) orow[j] = 0.0;
+        for (int i = 0; i < f; ++i) {
+          double dh = 0.0;
+          for (int j = 0; j < d; ++j) {
+            const double w = (double)elem(w2, dtype, w2b + (int64_t)i * d + j);
+            orow[j] += h[i] * w;
+            dh += w * go[j];
+            dw2[w2b + (int64_t)i * d + j] += h[i] * go[j];
+          }
+          dz[i] = dh * act_grad(act, z[i]);
+        }
+        double* dxr = dx_rows + r * d;
+        for (int j = 0; j < d; ++j) {
+          double s = 0.0;
+          for (int i = 0; i < f; ++i) {
+            s += (double)elem(w1, dtype, w1b + (int64_t)j * f + i) * dz[i];
+            dw1[w1b + (int64_t)j * f + i] += xr[j] * dz[i];
+          }
+          dxr[j] = s;
+        }
+      }
+    }
+    free(xr);
+    free(z);
+    free(h);
+    free(dz);
+  }
+}
+
+/* Gate backward, fp64, per token. Inputs: the gate's H, clean and sigma     */
+/* (noisy) [T,E] as the forward computed them, its noise eps [T,E], the     */
+/* order [T,kk] (first kk experts, kk = min(k+1, E) when noisy, else k), the */
+/* gates g [T,k] and dL/dg [T,k] (all k assignments, kept or dropped: the   */
+/* caller folds in the importance loss), the routed counts and the loss     */
+/* weight w_switch of E * sum_e f_e P_e, and dL/dLoad [E] (noisy). Writes   */
+/* dclean [T,E] = dL/d(x W_g + b) and, noisy, du [T,E] = dL/d(x W_noise).   */
+/*   renormalize: g = softmax over the kept logits -> dH_{e_s} +=            */
+/*     g_s (dg_s - sum_s' g_s' dg_s');                                       */
+/*   raw: g_s = p_{e_s} with p = softmax(H) over all E: dp_{e_s} += dg_s;    */
+/*   switch loss: dp_j += w_switch * E * f_j / T; then dH_j += p_j (dp_j -   */
+/*     sum_i p_i dp_i);                                                     */
+/*   load: P(t,e) = Phi((clean_e - H_{j*}) / sigma_e), j* the expert whose  */
+/*     H is kth_excluding(H, k, e) (none when e is kept and k = E):         */
+/*     c = dLoad_e phi(z) / sigma_e -> dclean_e += c, dH_{j*} -= c,          */
+/*     dsigma_e -= c z;                                                     */
+/*   H = clean + eps sigma -> dclean += dH, dsigma += eps dH;               */
+/*   sigma = softplus(u), sigmoid(u) = 1 - exp(-sigma) -> du = dsigma (1 -   */
+/*     exp(-sigma)).                                                         */
+void oracle_gate_bwd(int64_t T, int E, int k, int renormalize, const float* H, const float* clean, const float* sigma,
+                     const float* eps, const int32_t* order, int kk, const double* g, const double* dg,
+                     const int32_t* counts_routed, double w_switch, const double* dload, double* dclean, double* du) {
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)E);
+    double* dH = (double*)malloc(sizeof(double) * (size_t)E);
+    double* dcl = (double*)malloc(sizeof(double) * (size_t)E);
+    double* dsig = (double*)malloc(sizeof(double) * (size_t)E);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      const float* h = H + t * E;
+      const int32_t* o = order + t * kk;
+      double m = -INFINITY;
+      for (int e = 0; e < E; ++e)
+        if ((double)h[e] > m) m = h[e];
+      double zsum = 0.0;
+      for (int e = 0; e < E; ++e) zsum += exp((double)h[e] - m);
+      for (int e = 0; e < E; ++e) {
+        p[e] = exp((double)h[e] - m) / zsum;
+        dp[e] = dH[e] = dcl[e] = dsig[e] = 0.0;
+      }
+      const double* gt = g + t * k;
+      const double* dgt = dg + t * k;
+      if (renormalize) {
+        double s = 0.0;
+        for (int q = 0; q < k; ++q) s += gt[q] * dgt[q];
+        for (int q = 0; q < k; ++q) dH[o[q]] += gt[q] * (dgt[q] - s);
+      } else {
+        for (int q = 0; q < k; ++q) dp[o[q]] += dgt[q];
+      }
+      if (w_switch != 0.0)
+        for (int e = 0; e < E; ++e)
+          dp[e] += w_switch * (double)E * ((double)counts_routed[e] / ((double)T * (double)k)) / (double)T;
+      double sp = 0.0;
+      for (int e = 0; e < E; ++e) sp += p[e] * dp[e];
+      for (int e = 0; e < E; ++e) dH[e] += p[e] * (dp[e] - sp);
+      if (sigma && dload) {
+        for (int e = 0; e < E; ++e) {
+          int in_topk = 0;
+          for (int q = 0; q < k; ++q)
+            if (o[q] == e) in_topk = 1;
+          if (in_topk && kk <= k) continue; /* k == E: P = 1, no gradient */
+          const int js = in_topk ? o[k] : o[k - 1];
+          const double sg = sigma[t * E + e];
+          const double zz = ((double)clean[t * E + e] - (double)h[js]) / sg;
+          const double c = dload[e] * exp(-0.5 * zz * zz) / sqrt(2.0 * ORACLE_PI) / sg;
+          dcl[e] += c;
+          dH[js] -= c;
+          dsig[e] -= c * zz;
+        }
+      }
+      for (int e = 0; e < E; ++e) {
+        dclean[t * E + e] = dcl[e] + dH[e];
+        if (sigma) {
+          const double ds = dsig[e] + (double)eps[t * E + e] * dH[e];
+          du[t * E + e] = ds * (1.0 - exp(-(double)sigma[t * E + e]));
+        }
+      }
+    }
+    free(p);
+    free(dp);
+    free(dH);
+    free(dcl);
+    free(dsig);
   }
 }

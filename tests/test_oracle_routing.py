@@ -247,6 +247,62 @@ def test_dispatch_sequential_simulation(orc):
             assert out["slot_dest"][t, s] == want
 
 
+def _slot_major_walk(idx, E, C):
+    """First-choice priority by brute force: serve every token's first choice
+    (in token order), then every token's second choice, and so on; each
+    assignment takes its expert's next rank; rank >= C is dropped."""
+    T, k = idx.shape
+    fill = [0] * E
+    rank = {}
+    for s in range(k):
+        for t in range(T):
+            e = int(idx[t, s])
+            rank[(t, s)] = fill[e]
+            fill[e] += 1
+    return fill, rank
+
+
+@pytest.mark.parametrize("T,E,k,C", [(400, 6, 2, 70), (300, 5, 3, 40), (64, 8, 8, 5), (50, 4, 1, 7),
+                                     (200, 9, 2, -1), (100, 3, 2, 0)])
+def test_dispatch_first_choice_priority_walk(orc, T, E, k, C):
+    rng = np.random.default_rng(T * 7 + k)
+    H = rng.standard_normal((T, E)).astype(np.float32)
+    H[:, 1] += 1.5  # a hot expert: many first choices land on it, capacity binds there first
+    idx = orc.topk_order(H, k)
+    out = orc.dispatch(idx, E, C, slot_major=True)
+    fill, rank = _slot_major_walk(idx, E, C)
+    assert list(out["counts_routed"]) == fill
+    kept = [min(c, C) if C >= 0 else c for c in fill]
+    assert list(out["counts_kept"]) == kept
+    assert list(out["offsets"]) == list(np.concatenate([[0], np.cumsum(kept)]))
+    for t in range(T):
+        for s in range(k):
+            e = int(idx[t, s])
+            r = rank[(t, s)]
+            want = int(out["offsets"][e]) + r if (C < 0 or r < C) else -1
+            assert out["slot_dest"][t, s] == want
+            if want >= 0:
+                assert out["row_src"][want] == t
+    # the defining property: a first choice is dropped only if its expert's capacity
+    # is filled by first choices alone
+    first = idx[:, 0]
+    n_first = np.bincount(first, minlength=E)
+    dropped_first = out["slot_dest"][:, 0] < 0
+    if C >= 0:
+        assert np.all(n_first[first[dropped_first]] > C)
+    else:
+        assert not dropped_first.any()
+
+
+def test_first_choice_priority_equals_token_order_for_top1(orc):
+    rng = np.random.default_rng(9)
+    idx = orc.topk_order(rng.standard_normal((500, 7)).astype(np.float32), 1)
+    a = orc.dispatch(idx, 7, 40)
+    b = orc.dispatch(idx, 7, 40, slot_major=True)
+    for key in ("counts_kept", "offsets", "slot_dest", "row_src"):
+        assert np.array_equal(a[key], b[key])
+
+
 def test_zero_gate_weights_route_everything_to_expert_zero(orc):
     """W_g = 0: all logits tie, the lower index wins, so every token picks
     expert 0 first; with capacity C exactly C are kept, T - C dropped."""
