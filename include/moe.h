@@ -167,6 +167,23 @@ moe_status moe_dispatch(const moe_params* p, const void* x, const int32_t* topk_
                         size_t ws_bytes, void* stream);
 
 /*
+ * moe_dispatch_noalloc -- moe_dispatch with no workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Same inputs, outputs,
+ * layouts and results as moe_dispatch.
+ * Its scratch (the per-block expert counts) lives in a fixed 1 MiB device array
+ * inside the library, one copy per GPU, held until the process ends; the first
+ * call on a device looks up that device's copy. The call allocates nothing.
+ * Limit: E * ceil(T*k / 1024) * 4 bytes (rounded up to 256) <= 1 MiB, else
+ * MOE_ERR_UNSUPPORTED before anything is enqueued (e.g. E = 256 allows
+ * T*k <= 1,048,576). Every call on a GPU shares that GPU's array: calls that
+ * may overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller. Nothing in the array needs to start at zero.
+ */
+moe_status moe_dispatch_noalloc(const moe_params* p, const void* x, const int32_t* topk_idx, int32_t* counts_kept,
+                                int32_t* offsets, int32_t* slot_dest, int32_t* row_src, void* x_perm, void* stream);
+
+/*
  * moe_expert_ffn -- every expert's two-layer FFN on its contiguous row segment.
  *   (Shazeer abstract / "Methode": experts are feed-forward sub-networks.)
  *   y_perm[r] = act(x_perm[r] . w1[e]) . w2[e] for offsets[e] <= r < offsets[e+1],

@@ -28,7 +28,7 @@ MOE_GATE_AUTO, MOE_GATE_CANONICAL, MOE_GATE_FALLBACK = range(3)
 EXPORTED = (
     "moe_status_string", "moe_last_error", "moe_capacity", "moe_max_rows", "moe_workspace_size",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_canonical_softplus",
-    "moe_set_phase_events",
+    "moe_set_phase_events", "moe_dispatch_noalloc",
 )
 
 
@@ -82,6 +82,7 @@ def _load():
         "moe_forward": ([PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
         "moe_canonical_softplus": ([P, P, i64, P], i32),
         "moe_set_phase_events": ([ctypes.POINTER(P), i32], i32),
+        "moe_dispatch_noalloc": ([PP, P, P, P, P, P, P, P, P], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -169,6 +170,12 @@ def moe_dispatch(p, x, topk_idx, counts_kept, offsets, slot_dest, row_src, x_per
     wp, wn = _ws(ws)
     _check(lib().moe_dispatch(ctypes.byref(p), _ptr(x), _ptr(topk_idx), _ptr(counts_kept), _ptr(offsets),
                              _ptr(slot_dest), _ptr(row_src), _ptr(x_perm), wp, wn, _stream(stream)), "moe_dispatch")
+
+
+def moe_dispatch_noalloc(p, x, topk_idx, counts_kept, offsets, slot_dest, row_src, x_perm, stream=None):
+    _check(lib().moe_dispatch_noalloc(ctypes.byref(p), _ptr(x), _ptr(topk_idx), _ptr(counts_kept), _ptr(offsets),
+                                      _ptr(slot_dest), _ptr(row_src), _ptr(x_perm), _stream(stream)),
+           "moe_dispatch_noalloc")
 
 
 def moe_expert_ffn(p, x_perm, offsets, w1, w2, y_perm, ws=None, stream=None):

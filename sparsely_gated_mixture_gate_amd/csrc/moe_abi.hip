@@ -6,10 +6,18 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "moe.h"
 #include "common.h"
+
+// Scratch of moe_dispatch_noalloc (the per-block expert counts of the dispatch):
+// a fixed device array, one copy per GPU, held until the process ends. Host code
+// never uses this name as an address: it looks up each device's copy with
+// hipGetSymbolAddress (scratch_address below) and passes that pointer on.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
 
 hipError_t launch_softplus(const float* z, float* out, int64_t n, hipStream_t s);
 
@@ -334,6 +342,43 @@ moe_status run_combine(const moe_params* p, const void* y_perm, const int32_t* s
   return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
 }
 
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+moe_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device ordinal %d >= 64", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t se = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (se != hipSuccess) return hip_fail(se, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return MOE_OK;
+}
+
+moe_status check_dispatch_args(const moe_params* p, const void* x, const int32_t* topk_idx, int32_t* counts_kept,
+                               int32_t* offsets, int32_t* slot_dest, int32_t* row_src, void* x_perm) {
+  moe_status st = check_params(p);
+  if (st != MOE_OK) return st;
+  REQUIRE_PTR(counts_kept, "counts_kept");
+  REQUIRE_PTR(offsets, "offsets");
+  if (p->T > 0) {
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(topk_idx, "topk_idx");
+    REQUIRE_PTR(slot_dest, "slot_dest");
+    REQUIRE_PTR(row_src, "row_src");
+    REQUIRE_PTR(x_perm, "x_perm");
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -394,18 +439,28 @@ moe_status moe_route(const moe_params* p, const void* x, const void* w_gate, con
 moe_status moe_dispatch(const moe_params* p, const void* x, const int32_t* topk_idx, int32_t* counts_kept,
                         int32_t* offsets, int32_t* slot_dest, int32_t* row_src, void* x_perm, void* ws,
                         size_t ws_bytes, void* stream) {
-  moe_status st = check_params(p);
+  moe_status st = check_dispatch_args(p, x, topk_idx, counts_kept, offsets, slot_dest, row_src, x_perm);
   if (st != MOE_OK) return st;
-  REQUIRE_PTR(counts_kept, "counts_kept");
-  REQUIRE_PTR(offsets, "offsets");
-  if (p->T > 0) {
-    REQUIRE_PTR(x, "x");
-    REQUIRE_PTR(topk_idx, "topk_idx");
-    REQUIRE_PTR(slot_dest, "slot_dest");
-    REQUIRE_PTR(row_src, "row_src");
-    REQUIRE_PTR(x_perm, "x_perm");
-  }
   if ((st = check_ws(p, MOE_OP_DISPATCH, false, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c(ws);
+  int32_t* blk = carve_dispatch(c, p);
+  return run_dispatch(p, x, topk_idx, counts_kept, offsets, slot_dest, row_src, x_perm, blk, nullptr, false, nullptr,
+                      static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_dispatch_noalloc(const moe_params* p, const void* x, const int32_t* topk_idx, int32_t* counts_kept,
+                                int32_t* offsets, int32_t* slot_dest, int32_t* row_src, void* x_perm, void* stream) {
+  moe_status st = check_dispatch_args(p, x, topk_idx, counts_kept, offsets, slot_dest, row_src, x_perm);
+  if (st != MOE_OK) return st;
+  const size_t need = ws_bytes_for(p, MOE_OP_DISPATCH, false);
+  if (need > kNoAllocScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "the dispatch needs %zu bytes of scratch (E * ceil(T*k/1024) counts), more than the %zu-byte static "
+                "scratch of moe_dispatch_noalloc",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MOE_OK) return st;
+  // every count the kernels read is written earlier in the same call: nothing to clear
   Carver c(ws);
   int32_t* blk = carve_dispatch(c, p);
   return run_dispatch(p, x, topk_idx, counts_kept, offsets, slot_dest, row_src, x_perm, blk, nullptr, false, nullptr,
