@@ -27,7 +27,6 @@ from __future__ import annotations
 import argparse
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -241,14 +240,20 @@ def stats_report(path):
 
 
 def gpu_clock():
-    """Current and maximum shader clock reported by rocm-smi (a child process), or None."""
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        data = json.loads(r.stdout)
-        card = next(iter(data.values()))
-        return {k: v for k, v in card.items() if "sclk" in k.lower() or "fclk" in k.lower() or "mclk" in k.lower()}
-    except Exception:  # noqa: BLE001 -- informational only
-        return None
+    """Shader clock levels from sysfs (the current one marked '*'), read right after
+    the timed loops; a file read, no child process. None where sysfs does not show them."""
+    import glob
+
+    out = {}
+    for fn in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            levels = open(fn).read().split("\n")
+        except OSError:
+            continue
+        cur = [ln.strip() for ln in levels if ln.strip().endswith("*")]
+        out[fn.split("/")[4]] = {"current": cur[0] if cur else None,
+                                 "levels": [ln.strip() for ln in levels if ln.strip()]}
+    return out or None
 
 
 # --------------------------------------------------------------------------
@@ -445,7 +450,7 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
-    from synthetic import CONFIG_ORDER
+    from synthetic.configs import CONFIG_ORDER
 
     for name in (CONFIG_ORDER if args.config == "all" else [args.config]):
         run_config(args, name)

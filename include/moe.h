@@ -60,8 +60,12 @@ typedef enum moe_status {
 
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 enum { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1 }; /* GELU is the exact 0.5 z (1 + erf(z / sqrt 2)) */
-enum { MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2, MOE_OP_FORWARD = 3 };
+enum {
+  MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2, MOE_OP_FORWARD = 3, MOE_OP_BACKWARD = 4,
+  MOE_OP_ROUTE_HIER = 5, MOE_OP_FORWARD_HIER = 6
+};
 enum { MOE_GATE_AUTO = 0, MOE_GATE_CANONICAL = 1, MOE_GATE_FALLBACK = 2 };
+enum { MOE_DROP_TOKEN_ORDER = 0, MOE_DROP_FIRST_CHOICE = 1 };
 
 typedef struct moe_params {
   int64_t T;               /* tokens in the batch */
@@ -83,6 +87,19 @@ typedef struct moe_params {
                                 canonical fallback (testing). Routing is identical in all modes. */
   double capacity_factor;  /* > 0: per-expert capacity C = ceil(capacity_factor * k * T / E); <= 0: none */
   int64_t capacity;        /* >= 0: explicit per-expert capacity C (overrides capacity_factor); < 0: unused */
+  int32_t drop_order;      /* which assignments a full expert drops (MOE_DROP_*):
+                              MOE_DROP_TOKEN_ORDER (0): tokens in order, slots in order within a token;
+                                the first C assignments of an expert are kept;
+                              MOE_DROP_FIRST_CHOICE (1): first-choice priority ("moe paper models"
+                                table 2, GShard row: top-2 with a capacity): slot 0 of every token in
+                                token order, then slot 1 of every token, ...; ranks and the rows of
+                                each expert's segment follow that order. Same as 0 when k = 1. */
+  int32_t groups;          /* hierarchical layers (moe_route_hier / moe_forward_hier): the number of
+                              secondary MoE groups g >= 1, each of E / g experts; 0 or 1 for a flat
+                              layer (the flat gate's entry points reject groups > 1) */
+  int32_t k_group;         /* hierarchical layers: groups the primary gate keeps (k_group <= groups);
+                              each kept group keeps k / k_group of its experts, so k is the total
+                              number of expert slots of a token */
 } moe_params;
 
 /* Human-readable name of a status code. Never NULL; static storage. */
@@ -152,15 +169,16 @@ moe_status moe_route(const moe_params* p, const void* x, const void* w_gate, con
  * moe_dispatch -- group assignments by expert with capacity drops in token order.
  *   (Switch listing: per-expert gather of the routed tokens; "moe paper
  *    models" table 2: capacity factors.)
- * The T*k assignments are walked in token order (slot order within a token);
- * each takes the next rank of its expert; rank >= C is dropped.
+ * The T*k assignments are walked in token order (slot order within a token),
+ * or slot-major with drop_order = MOE_DROP_FIRST_CHOICE; each takes the next
+ * rank of its expert; rank >= C is dropped.
  * Inputs:  x [T,d] dtype; topk_idx [T,k] int32 (values in [0,E), distinct per token).
  * Outputs: counts_kept [E] int32 = min(routed_e, C);
  *          offsets [E+1] int32, exclusive prefix sum of counts_kept (offsets[E] = R);
  *          slot_dest [T,k] int32: row of the assignment in x_perm, or -1 if dropped;
  *          row_src [moe_max_rows] int32: token of each row (entries >= R untouched);
  *          x_perm [moe_max_rows, d] dtype: x_perm[r] = x[row_src[r]] (rows >= R untouched).
- * Rows are sorted by (expert, token).
+ * Rows are sorted by (expert, token), or (expert, slot, token) with first-choice priority.
  */
 moe_status moe_dispatch(const moe_params* p, const void* x, const int32_t* topk_idx, int32_t* counts_kept,
                         int32_t* offsets, int32_t* slot_dest, int32_t* row_src, void* x_perm, void* ws,
@@ -224,6 +242,88 @@ moe_status moe_forward(const moe_params* p, const void* x, const void* w_gate, c
                        const void* w_noise, const float* noise, const void* w1, const void* w2, void* y,
                        float* aux_out, int32_t* topk_idx, float* topk_gate, int32_t* counts_routed,
                        int32_t* counts_kept, int32_t* slot_dest, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_hier -- the gate of a hierarchical MoE layer.
+ *   (Shazeer summary page, "Schluesselbegriffe": a primary gating network routes
+ *    each input to secondary MoE groups; "moe paper models" table 2: k = 2 for
+ *    the hierarchical models.)
+ * The layer is a MoE of MoEs, y = sum_i Gp(x)_i sum_j G_i(x)_j E_ij(x), with both
+ * gates noisy top-k gates of the "Methode" section (softmax over the kept logits):
+ *   primary:   Hp = x w_gate_p (+ gate_bias_p) (+ noise_p * softplus(x w_noise_p)),
+ *              over p->groups groups, keeps p->k_group of them;
+ *   secondary: Hs = x w_gate_s (+ gate_bias_s) (+ noise_s * softplus(x w_noise_s)),
+ *              over all E experts (column g * b + j is expert j of group g,
+ *              b = E / groups); each kept group keeps its top k / k_group.
+ * Logits are the canonical fp32 chains of moe_route; top-k ties go to the lower
+ * index. Slot r * (k / k_group) + q of a token is expert q of its r-th kept group:
+ * topk_idx = g * b + j, topk_gate = Gp_g * G_g,j. moe_dispatch, moe_expert_ffn
+ * and moe_combine then treat the layer as a flat one with E experts and k slots.
+ * Inputs:  x [T,d] dtype; w_gate_p [d,groups], w_gate_s [d,E] dtype; gate_bias_p
+ *          [groups], gate_bias_s [E] fp32 or NULL; w_noise_p [d,groups] + noise_p
+ *          [T,groups] and w_noise_s [d,E] + noise_s [T,E] (fp32 standard normals),
+ *          each pair both or neither.
+ * Outputs: topk_idx, topk_gate [T,k]; counts_routed [E]; aux_out [3] or NULL:
+ *          {CV^2 of the primary importance (per group), CV^2 of the importance of
+ *          the combined gates (per expert), CV^2 of the primary load estimate
+ *          (NaN without w_noise_p)} (population CV, unweighted).
+ * Requires groups >= 1 dividing E, k_group >= 1 dividing k, k_group <= groups,
+ * k / k_group <= E / groups. renormalize and gate_mode are not used.
+ * Workspace: moe_workspace_size(p, MOE_OP_ROUTE_HIER).
+ */
+moe_status moe_route_hier(const moe_params* p, const void* x, const void* w_gate_p, const float* gate_bias_p,
+                          const void* w_noise_p, const float* noise_p, const void* w_gate_s, const float* gate_bias_s,
+                          const void* w_noise_s, const float* noise_s, int32_t* topk_idx, float* topk_gate,
+                          int32_t* counts_routed, float* aux_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_forward_hier -- the whole hierarchical layer: moe_route_hier, then the
+ * dispatch, expert FFN and combine of moe_forward (E experts, k slots).
+ * Inputs as moe_route_hier plus w1 [E,d,f], w2 [E,f,d]; outputs as moe_forward
+ * (aux_out as moe_route_hier). Workspace: moe_workspace_size(p, MOE_OP_FORWARD_HIER).
+ */
+moe_status moe_forward_hier(const moe_params* p, const void* x, const void* w_gate_p, const float* gate_bias_p,
+                            const void* w_noise_p, const float* noise_p, const void* w_gate_s,
+                            const float* gate_bias_s, const void* w_noise_s, const float* noise_s, const void* w1,
+                            const void* w2, void* y, float* aux_out, int32_t* topk_idx, float* topk_gate,
+                            int32_t* counts_routed, int32_t* counts_kept, int32_t* slot_dest, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * moe_backward -- gradients of the layer (the pages train it: Shazeer
+ *   "Fragen" -- the top-k is taken before the softmax, so the kept gate values
+ *   keep continuous derivatives and gradients reach the gate; "Kernideen" --
+ *   the noise term keeps them smooth; "Load-Balancing-Losses").
+ * Loss: L = sum(dy * y) + w_switch * aux[0] + w_importance * aux[1] +
+ * w_load * aux[2] (aux as moe_route; w_load only with w_noise), with y the
+ * layer output of moe_forward on the same inputs and parameters. The discrete
+ * choices -- top-k sets (the canonical routing), ranks, capacity drops -- are
+ * held fixed; everything else is differentiated:
+ *   experts:  dW2[e] = sum over e's kept rows of act(z)^T (g dy_t),
+ *             dW1[e] = sum of x_t^T dz, dz = ((g dy_t) W2[e]^T) * act'(z);
+ *   gate:     dL/dg = <dy_t, expert output> (kept) + the importance term;
+ *             through Softmax(KeepTopK) (renormalize = 1) or the full softmax
+ *             (0, and the switch loss), the load estimator's Phi terms (its
+ *             threshold's gradient goes to the expert holding kth_excluding),
+ *             H = clean + noise * softplus(x W_noise);
+ *   inputs:   dx_t = sum of the row gradients of its kept slots + dclean_t W_gate^T
+ *             (+ du_t W_noise^T).
+ * The layer is recomputed inside (routing, dispatch, both expert layers), so
+ * only the forward's inputs are needed.
+ * Inputs as moe_forward, plus dy [T,d] dtype and the three loss weights (host
+ * doubles, finite; 0 leaves a loss out).
+ * Outputs: dx [T,d] dtype; dw_gate [d,E] fp32; dgate_bias [E] fp32 (written iff
+ *          gate_bias and dgate_bias are both non-NULL); dw_noise [d,E] fp32
+ *          (required iff w_noise); dw1 [E,d,f] and dw2 [E,f,d] dtype (experts
+ *          with no rows get zeros); dlogits [T,E] fp32 or NULL: dL/d(clean
+ *          logits x W_gate + b).
+ * Workspace: moe_workspace_size(p, MOE_OP_BACKWARD).
+ */
+moe_status moe_backward(const moe_params* p, const void* x, const void* w_gate, const float* gate_bias,
+                        const void* w_noise, const float* noise, const void* w1, const void* w2, const void* dy,
+                        double w_switch, double w_importance, double w_load, void* dx, float* dw_gate,
+                        float* dgate_bias, float* dw_noise, void* dw1, void* dw2, float* dlogits, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /*
  * moe_set_phase_events -- phase timing of moe_forward (a measurement aid; the

@@ -57,7 +57,7 @@ def _lib():
             "oracle_expert_ffn_rows": ([i64, i32, i32, i32, i32, P, P, P, P, P, P], None),
             "oracle_combine": ([i64, P, i32, i32, P, P, P, P, P], None),
             "oracle_expert_bwd_rows": ([i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P], None),
-            "oracle_gate_bwd": ([i64, i32, i32, i32, P, P, P, P, P, i32, P, P, P, dbl, P, P, P], None),
+            "oracle_gate_bwd": ([i64, i64, i32, i32, i32, P, P, P, P, P, i32, P, P, P, dbl, P, P, P], None),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(lib, name)
@@ -277,7 +277,16 @@ def forward(spec: LayerSpec, inp: dict, tokens=None) -> dict:
     r = route(spec, inp)
     C = capacity(spec.T, spec.E, spec.k, spec.capacity_factor, spec.capacity)
     disp = dispatch(r["topk_idx"], spec.E, C, spec.slot_major)
-    T, k = spec.T, spec.k
+    out = dict(r)
+    out.update(disp)
+    out.update(_experts_and_combine(spec, inp, r["topk_idx"], r["topk_gate"], disp, tokens))
+    out.update(C=C)
+    return out
+
+
+def _experts_and_combine(spec, inp, topk_idx, topk_gate, disp, tokens):
+    """Each kept assignment's expert FFN output, gate-weighted and summed per token."""
+    T, k = spec.T, topk_idx.shape[1]
     if tokens is None:
         tokens = np.arange(T, dtype=np.int32)
     tokens = np.asarray(tokens, dtype=np.int32)
@@ -285,16 +294,92 @@ def forward(spec: LayerSpec, inp: dict, tokens=None) -> dict:
     kept = slots >= 0
     rows_slot = slots[kept]
     rows_tok = np.repeat(tokens, k).reshape(-1, k)[kept]
-    rows_exp = r["topk_idx"][tokens][kept]
+    rows_exp = topk_idx[tokens][kept]
     yp = expert_ffn_rows(inp["x"], rows_tok, rows_exp, inp["w1"], inp["w2"], spec.act, spec.dtype)
     R = disp["R"]
     row_of_slot = np.full(max(R, 1), -1, np.int32)
     row_of_slot[rows_slot] = np.arange(rows_slot.shape[0], dtype=np.int32)
-    y = combine(tokens, disp["slot_dest"], r["topk_gate"], yp if yp.size else np.zeros((1, spec.d_model)),
-                row_of_slot)
+    y = combine(tokens, disp["slot_dest"], topk_gate, yp if yp.size else np.zeros((1, spec.d_model)), row_of_slot)
+    return dict(tokens=tokens, y=y, yp=yp, yp_slots=rows_slot)
+
+
+# --------------------------------------------------------------------------
+# hierarchical MoE (Shazeer et al. summary page, "Schluesselbegriffe": a primary
+# gating network routes each input to secondary MoE groups; "moe paper models"
+# table 2: k = 2 for the hierarchical models). Reading: the layer is a MoE of
+# MoEs, y = sum_i Gp(x)_i sum_j G_i(x)_j E_ij(x), each gate a (noisy) top-k gate
+# of the "Methode" section with the softmax over its kept logits; the expert
+# slots of a token are (kept group r, kept expert q of that group) in that order,
+# expert id i * b + j, gate Gp_i * G_i,j. Losses: CV^2 of the primary importance
+# (per group), CV^2 of the importance of the combined gates (per expert), CV^2 of
+# the primary load (noisy primary gate; else NaN).
+# --------------------------------------------------------------------------
+@dataclass
+class HierSpec:
+    T: int
+    d_model: int
+    d_ff: int
+    groups: int
+    experts_per_group: int
+    k_group: int
+    k: int
+    dtype: str
+    act: str
+    capacity_factor: float = 0.0
+    capacity: int = -1
+
+    @property
+    def E(self) -> int:
+        return self.groups * self.experts_per_group
+
+    @property
+    def slots(self) -> int:
+        return self.k_group * self.k
+
+    @classmethod
+    def of(cls, cfg, capacity: int = -1) -> "HierSpec":
+        return cls(cfg.T, cfg.d_model, cfg.d_ff, cfg.groups, cfg.experts_per_group, cfg.k_group, cfg.k, cfg.dtype,
+                   cfg.act, float(cfg.capacity_factor), int(capacity))
+
+
+def route_hier(spec: HierSpec, inp: dict) -> dict:
+    T, a, b, kp, ks, E = spec.T, spec.groups, spec.experts_per_group, spec.k_group, spec.k, spec.E
+    clean_p, sig_p, Hp = gate_logits(inp["x"], inp["w_gate_p"], inp.get("gate_bias_p"), inp.get("w_noise_p"),
+                                     inp.get("noise_p"), spec.dtype)
+    clean_s, sig_s, Hs = gate_logits(inp["x"], inp["w_gate_s"], inp.get("gate_bias_s"), inp.get("w_noise_s"),
+                                     inp.get("noise_s"), spec.dtype)
+    noisy_p = inp.get("w_noise_p") is not None
+    order_p = topk_order(Hp, min(kp + 1, a) if noisy_p else kp)
+    top_p = np.ascontiguousarray(order_p[:, :kp])
+    gp, _ = gates(Hp, top_p, True, want_prob=False)
+    # each kept group's own top-k over its b experts, softmax over the kept logits
+    Hsel = np.ascontiguousarray(Hs.reshape(T, a, b)[np.arange(T)[:, None], top_p].reshape(T * kp, b))
+    js = topk_order(Hsel, ks)
+    gs, _ = gates(Hsel, js, True, want_prob=False)
+    topk_idx = (top_p[:, :, None] * b + js.reshape(T, kp, ks)).reshape(T, kp * ks).astype(np.int32)
+    topk_gate = (gp[:, :, None] * gs.reshape(T, kp, ks)).reshape(T, kp * ks)
+    counts_routed = np.bincount(topk_idx.ravel(), minlength=E).astype(np.int32)
+    imp_p = np.zeros(a, np.float64)
+    np.add.at(imp_p, top_p.ravel(), gp.ravel())
+    imp_c = np.zeros(E, np.float64)
+    np.add.at(imp_c, topk_idx.ravel(), topk_gate.ravel())
+    load_p = load(clean_p, sig_p, Hp, order_p, kp) if noisy_p else None
+    counts_p = np.bincount(top_p.ravel(), minlength=a).astype(np.int32)
+    a_p = aux(T, kp, counts_p, np.zeros(a), imp_p, load_p)
+    a_c = aux(T, kp * ks, counts_routed, np.zeros(E), imp_c)
+    return dict(Hp=Hp, Hs=Hs, clean_p=clean_p, sigma_p=sig_p, order_p=order_p, gate_p=gp, topk_idx=topk_idx,
+                topk_gate=topk_gate, counts_routed=counts_routed, importance_p=imp_p, importance=imp_c,
+                load_p=load_p, aux=np.array([a_p[1], a_c[1], a_p[2]]))
+
+
+def forward_hier(spec: HierSpec, inp: dict, tokens=None) -> dict:
+    r = route_hier(spec, inp)
+    C = capacity(spec.T, spec.E, spec.slots, spec.capacity_factor, spec.capacity)
+    disp = dispatch(r["topk_idx"], spec.E, C)
     out = dict(r)
     out.update(disp)
-    out.update(C=C, tokens=tokens, y=y, yp=yp, yp_slots=rows_slot)
+    out.update(_experts_and_combine(spec, inp, r["topk_idx"], r["topk_gate"], disp, tokens))
+    out.update(C=C)
     return out
 
 
@@ -303,9 +388,10 @@ def forward(spec: LayerSpec, inp: dict, tokens=None) -> dict:
 # "Fragen" -- gradients flow through the kept gates because the top-k is taken
 # before the softmax; "Kernideen" -- the noise term keeps them smooth)
 # --------------------------------------------------------------------------
-def expert_bwd_rows(x, x_row, expert, w1, w2, dout, act: str, dtype: str):
+def expert_bwd_rows(x, x_row, expert, w1, w2, dout, act: str, dtype: str, want_dw: bool = True):
     """fp64 expert FFN backward for rows r (expert[r] applied to x[x_row[r]])
-    with upstream gradient dout[r]. Returns (o, dx_rows, dw1, dw2)."""
+    with upstream gradient dout[r]. Returns (o, dx_rows, dw1, dw2); dw1 / dw2
+    are None with want_dw=False."""
     wd = _wdtype(dtype)
     x, w1, w2 = _c(x, wd), _c(w1, wd), _c(w2, wd)
     x_row, expert = _c(x_row, np.int32), _c(expert, np.int32)
@@ -314,16 +400,17 @@ def expert_bwd_rows(x, x_row, expert, w1, w2, dout, act: str, dtype: str):
     E, _, f = w1.shape
     o = np.zeros((n, d), np.float64)
     dx_rows = np.zeros((n, d), np.float64)
-    dw1 = np.empty((E, d, f), np.float64)
-    dw2 = np.empty((E, f, d), np.float64)
+    dw1 = np.empty((E, d, f), np.float64) if want_dw else None
+    dw2 = np.empty((E, f, d), np.float64) if want_dw else None
     _lib().oracle_expert_bwd_rows(n, d, f, E, _dcode(dtype), RELU if act == "relu" else GELU, _p(x), _p(x_row),
                                   _p(expert), _p(w1), _p(w2), _p(dout), _p(o), _p(dx_rows), _p(dw1), _p(dw2))
     return o, dx_rows, dw1, dw2
 
 
 def gate_bwd(H, clean, sigma, noise, order, k: int, renormalize: bool, g, dg, counts_routed, w_switch: float,
-             dload=None):
-    """dL/dclean [T,E] and (noisy) dL/d(x W_noise) [T,E], fp64."""
+             dload=None, T_batch=None):
+    """dL/dclean [T,E] and (noisy) dL/d(x W_noise) [T,E], fp64. The rows may be a
+    subset of a batch of T_batch tokens."""
     H, clean = _c(H, np.float32), _c(clean, np.float32)
     sigma, noise = _c(sigma, np.float32), _c(noise, np.float32)
     order = _c(order, np.int32)
@@ -333,7 +420,8 @@ def gate_bwd(H, clean, sigma, noise, order, k: int, renormalize: bool, g, dg, co
     T, E = H.shape
     dclean = np.empty((T, E), np.float64)
     du = np.empty((T, E), np.float64) if sigma is not None else None
-    _lib().oracle_gate_bwd(T, E, k, int(bool(renormalize)), _p(H), _p(clean), _p(sigma), _p(noise), _p(order),
+    _lib().oracle_gate_bwd(T, int(T if T_batch is None else T_batch), E, k, int(bool(renormalize)), _p(H), _p(clean),
+                           _p(sigma), _p(noise), _p(order),
                            order.shape[1], _p(g), _p(dg), _p(counts_routed), float(w_switch), _p(dload),
                            _p(dclean), _p(du))
     return dclean, du
@@ -350,45 +438,74 @@ def cv2_grad(v) -> np.ndarray:
     return 2.0 * (v - mu) / (E * mu * mu) - 2.0 * var / (E * mu ** 3)
 
 
-def backward(spec: LayerSpec, inp: dict, dy, loss_weights=(0.0, 0.0, 0.0)) -> dict:
+def backward(spec: LayerSpec, inp: dict, dy, loss_weights=(0.0, 0.0, 0.0), tokens=None, experts=None) -> dict:
     """Gradients of L = sum(dy * y) + w_switch * switch_aux + w_importance *
     CV(Importance)^2 + w_load * CV(Load)^2 with respect to x, W_gate, gate_bias,
     W_noise, W1 and W2, with the layer's discrete choices (top-k sets, capacity
-    drops) held fixed. fp64 throughout (logits: the forward's canonical fp32)."""
+    drops) held fixed. fp64 throughout (logits: the forward's canonical fp32).
+
+    ``tokens`` / ``experts`` (optional) restrict the work for large batches: the
+    expert FFN is evaluated only on the kept rows of the listed tokens and all
+    rows of the listed experts; dx, dclean and du then hold one row per listed
+    token, dw1 / dw2 map each listed expert to its gradients, and the gate weight
+    gradients (which need every token) are not formed. Routing, dispatch and
+    the batch statistics of the losses always cover the whole batch."""
     w_switch, w_imp, w_load = (float(w) for w in loss_weights)
     r = route(spec, inp)
     C = capacity(spec.T, spec.E, spec.k, spec.capacity_factor, spec.capacity)
     disp = dispatch(r["topk_idx"], spec.E, C, spec.slot_major)
     T, k, E = spec.T, spec.k, spec.E
+    subset = tokens is not None or experts is not None
+    tok_sel = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
     dy = np.asarray(dy, np.float64)
     kept = disp["slot_dest"] >= 0
     tok = np.repeat(np.arange(T, dtype=np.int32), k).reshape(T, k)
-    rows_tok, rows_exp = tok[kept], r["topk_idx"][kept]
+    want = np.zeros((T, k), bool)
+    want[tok_sel] = True
+    if experts is not None:
+        want |= np.isin(r["topk_idx"], np.asarray(experts))
+    use = kept & want if subset else kept
+    rows_tok, rows_exp = tok[use], r["topk_idx"][use]
     g = r["topk_gate"]
-    dout = g[kept][:, None] * dy[rows_tok]
+    dout = g[use][:, None] * dy[rows_tok]
     o, dx_rows, dw1, dw2 = expert_bwd_rows(inp["x"], rows_tok, rows_exp, inp["w1"], inp["w2"], dout, spec.act,
-                                           spec.dtype)
+                                           spec.dtype, want_dw=not subset)
+    if subset and experts is not None:
+        # weight gradients of the listed experts only, one expert at a time
+        dw1, dw2 = {}, {}
+        for e in np.asarray(experts):
+            m = use & (r["topk_idx"] == e)
+            _, _, a1, a2 = expert_bwd_rows(inp["x"], tok[m], np.zeros(int(m.sum()), np.int32),
+                                           inp["w1"][e:e + 1], inp["w2"][e:e + 1],
+                                           g[m][:, None] * dy[tok[m]], spec.act, spec.dtype)
+            dw1[int(e)], dw2[int(e)] = a1[0], a2[0]
     # dL/dg: the combine (kept slots only) plus the importance loss (all slots, pre-drop)
     dg = np.zeros((T, k), np.float64)
-    dg[kept] = np.einsum("rd,rd->r", dy[rows_tok], o)
+    dg[use] = np.einsum("rd,rd->r", dy[rows_tok], o)
     if w_imp:
         dg += w_imp * cv2_grad(r["importance"])[r["topk_idx"]]
     noisy = inp.get("w_noise") is not None
     dload = w_load * cv2_grad(r["load"]) if (noisy and w_load) else None
-    dclean, du = gate_bwd(r["H"], r["clean"], r["sigma"], inp.get("noise"), r["order"], k, spec.renormalize, g, dg,
-                          r["counts_routed"], w_switch, dload)
+    sel = lambda a: None if a is None else np.ascontiguousarray(a[tok_sel])  # noqa: E731
+    dclean, du = gate_bwd(sel(r["H"]), sel(r["clean"]), sel(r["sigma"]), sel(inp.get("noise")), sel(r["order"]), k,
+                          spec.renormalize, sel(g), sel(dg), r["counts_routed"], w_switch, dload, T_batch=T)
     xf = bf16_widen(inp["x"]) if spec.dtype == "bf16" else np.asarray(inp["x"], np.float64)
     wg = bf16_widen(inp["w_gate"]) if spec.dtype == "bf16" else np.asarray(inp["w_gate"], np.float64)
-    dx = np.zeros((T, spec.d_model), np.float64)
-    np.add.at(dx, rows_tok, dx_rows)
-    dx += dclean @ wg.T
-    out = dict(dx=dx, dw_gate=xf.T @ dclean, dw1=dw1, dw2=dw2, dg=dg, dclean=dclean, o=o, route=r, disp=disp,
-               dgate_bias=dclean.sum(axis=0) if inp.get("gate_bias") is not None else None,
-               dw_noise=None, du=du)
+    dx_all = np.zeros((T, spec.d_model), np.float64)
+    np.add.at(dx_all, rows_tok, dx_rows)
+    dx = dx_all[tok_sel] + dclean @ wg.T
+    out = dict(dx=dx, dw1=dw1, dw2=dw2, dg=dg, dclean=dclean, o=o, route=r, disp=disp, du=du, tokens=tok_sel,
+               dw_gate=None, dgate_bias=None, dw_noise=None)
     if noisy:
         wn = bf16_widen(inp["w_noise"]) if spec.dtype == "bf16" else np.asarray(inp["w_noise"], np.float64)
         dx += du @ wn.T
-        out["dw_noise"] = xf.T @ du
+    out["dx"] = dx
+    if not subset:
+        out["dw_gate"] = xf.T @ dclean
+        if inp.get("gate_bias") is not None:
+            out["dgate_bias"] = dclean.sum(axis=0)
+        if noisy:
+            out["dw_noise"] = xf.T @ du
     return out
 
 

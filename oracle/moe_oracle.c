@@ -487,12 +487,16 @@ static double act_grad(int act, double z) {
 /*   dh = W2[e] dout, dz = dh * act'(z), dx = W1[e] dz,                      */
 /*   dW2[e] += h^T dout, dW1[e] += x^T dz.                                   */
 /* Experts run in parallel; each expert's rows are taken in row order, so   */
-/* the sums do not depend on the thread count.                              */
+/* the sums do not depend on the thread count. dw1 = dw2 = NULL skips the   */
+/* weight gradients.                                                         */
 void oracle_expert_bwd_rows(int64_t n, int d, int f, int E, int dtype, int act, const void* x, const int32_t* x_row,
                             const int32_t* expert, const void* w1, const void* w2, const double* dout, double* o,
                             double* dx_rows, double* dw1, double* dw2) {
-  memset(dw1, 0, sizeof(double) * (size_t)E * d * f);
-  memset(dw2, 0, sizeof(double) * (size_t)E * f * d);
+  const int want_dw = dw1 != NULL && dw2 != NULL; /* NULL: outputs and dx only */
+  if (want_dw) {
+    memset(dw1, 0, sizeof(double) * (size_t)E * d * f);
+    memset(dw2, 0, sizeof(double) * (size_t)E * f * d);
+  }
 #pragma omp parallel
   {
     double* xr = (double*)malloc(sizeof(double) * (size_t)d);
@@ -520,7 +524,7 @@ void oracle_expert_bwd_rows(int64_t n, int d, int f, int E, int dtype, int act, 
             const double w = (double)elem(w2, dtype, w2b + (int64_t)i * d + j);
             orow[j] += h[i] * w;
             dh += w * go[j];
-            dw2[w2b + (int64_t)i * d + j] += h[i] * go[j];
+            if (want_dw) dw2[w2b + (int64_t)i * d + j] += h[i] * go[j];
           }
           dz[i] = dh * act_grad(act, z[i]);
         }
@@ -529,7 +533,7 @@ void oracle_expert_bwd_rows(int64_t n, int d, int f, int E, int dtype, int act, 
           double s = 0.0;
           for (int i = 0; i < f; ++i) {
             s += (double)elem(w1, dtype, w1b + (int64_t)j * f + i) * dz[i];
-            dw1[w1b + (int64_t)j * f + i] += xr[j] * dz[i];
+            if (want_dw) dw1[w1b + (int64_t)j * f + i] += xr[j] * dz[i];
           }
           dxr[j] = s;
         }
@@ -549,6 +553,8 @@ void oracle_expert_bwd_rows(int64_t n, int d, int f, int E, int dtype, int act, 
 /* caller folds in the importance loss), the routed counts and the loss     */
 /* weight w_switch of E * sum_e f_e P_e, and dL/dLoad [E] (noisy). Writes   */
 /* dclean [T,E] = dL/d(x W_g + b) and, noisy, du [T,E] = dL/d(x W_noise).   */
+/* The T rows may be a subset of the batch of T_batch tokens (the switch   */
+/* loss' f_e and P_e are batch means).                                      */
 /*   renormalize: g = softmax over the kept logits -> dH_{e_s} +=            */
 /*     g_s (dg_s - sum_s' g_s' dg_s');                                       */
 /*   raw: g_s = p_{e_s} with p = softmax(H) over all E: dp_{e_s} += dg_s;    */
@@ -561,9 +567,10 @@ void oracle_expert_bwd_rows(int64_t n, int d, int f, int E, int dtype, int act, 
 /*   H = clean + eps sigma -> dclean += dH, dsigma += eps dH;               */
 /*   sigma = softplus(u), sigmoid(u) = 1 - exp(-sigma) -> du = dsigma (1 -   */
 /*     exp(-sigma)).                                                         */
-void oracle_gate_bwd(int64_t T, int E, int k, int renormalize, const float* H, const float* clean, const float* sigma,
-                     const float* eps, const int32_t* order, int kk, const double* g, const double* dg,
-                     const int32_t* counts_routed, double w_switch, const double* dload, double* dclean, double* du) {
+void oracle_gate_bwd(int64_t T, int64_t T_batch, int E, int k, int renormalize, const float* H, const float* clean,
+                     const float* sigma, const float* eps, const int32_t* order, int kk, const double* g,
+                     const double* dg, const int32_t* counts_routed, double w_switch, const double* dload,
+                     double* dclean, double* du) {
 #pragma omp parallel
   {
     double* p = (double*)malloc(sizeof(double) * (size_t)E);
@@ -595,7 +602,7 @@ void oracle_gate_bwd(int64_t T, int E, int k, int renormalize, const float* H, c
       }
       if (w_switch != 0.0)
         for (int e = 0; e < E; ++e)
-          dp[e] += w_switch * (double)E * ((double)counts_routed[e] / ((double)T * (double)k)) / (double)T;
+          dp[e] += w_switch * (double)E * ((double)counts_routed[e] / ((double)T_batch * (double)k)) / (double)T_batch;
       double sp = 0.0;
       for (int e = 0; e < E; ++e) sp += p[e] * dp[e];
       for (int e = 0; e < E; ++e) dH[e] += p[e] * (dp[e] - sp);

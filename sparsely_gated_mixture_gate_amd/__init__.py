@@ -22,13 +22,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
-MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_FORWARD = range(4)
+(MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_FORWARD, MOE_OP_BACKWARD, MOE_OP_ROUTE_HIER,
+ MOE_OP_FORWARD_HIER) = range(7)
 MOE_GATE_AUTO, MOE_GATE_CANONICAL, MOE_GATE_FALLBACK = range(3)
+MOE_DROP_TOKEN_ORDER, MOE_DROP_FIRST_CHOICE = range(2)
 
 EXPORTED = (
     "moe_status_string", "moe_last_error", "moe_capacity", "moe_max_rows", "moe_workspace_size",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_canonical_softplus",
-    "moe_set_phase_events", "moe_dispatch_noalloc",
+    "moe_set_phase_events", "moe_dispatch_noalloc", "moe_backward", "moe_route_hier", "moe_forward_hier",
 )
 
 
@@ -51,6 +53,9 @@ class moe_params(ctypes.Structure):
         ("gate_mode", ctypes.c_int32),
         ("capacity_factor", ctypes.c_double),
         ("capacity", ctypes.c_int64),
+        ("drop_order", ctypes.c_int32),
+        ("groups", ctypes.c_int32),
+        ("k_group", ctypes.c_int32),
     ]
 
 
@@ -83,6 +88,10 @@ def _load():
         "moe_canonical_softplus": ([P, P, i64, P], i32),
         "moe_set_phase_events": ([ctypes.POINTER(P), i32], i32),
         "moe_dispatch_noalloc": ([PP, P, P, P, P, P, P, P, P], i32),
+        "moe_route_hier": ([PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
+        "moe_forward_hier": ([PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
+        "moe_backward": ([PP, P, P, P, P, P, P, P, P, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                          P, P, P, P, P, P, P, P, sz, P], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -134,11 +143,12 @@ def status_string(status: int) -> str:
 
 
 def make_params(T, d_model, d_ff, E, k, dtype="bf16", act="gelu", renormalize=False, capacity_factor=0.0,
-                capacity=-1, gate_mode=0) -> moe_params:
+                capacity=-1, gate_mode=0, drop_order=0, groups=0, k_group=0) -> moe_params:
     return moe_params(int(T), int(d_model), int(d_ff), int(E), int(k),
                       MOE_BF16 if dtype in ("bf16", MOE_BF16) else MOE_F32,
                       MOE_ACT_GELU if act in ("gelu", MOE_ACT_GELU) else MOE_ACT_RELU,
-                      int(bool(renormalize)), int(gate_mode), float(capacity_factor), int(capacity))
+                      int(bool(renormalize)), int(gate_mode), float(capacity_factor), int(capacity),
+                      int(drop_order), int(groups), int(k_group))
 
 
 def moe_capacity(p: moe_params) -> int:
@@ -196,6 +206,36 @@ def moe_forward(p, x, w_gate, gate_bias, w_noise, noise, w1, w2, y, aux_out=None
                             _ptr(w1), _ptr(w2), _ptr(y), _ptr(aux_out), _ptr(topk_idx), _ptr(topk_gate),
                             _ptr(counts_routed), _ptr(counts_kept), _ptr(slot_dest), wp, wn, _stream(stream)),
            "moe_forward")
+
+
+def moe_route_hier(p, x, w_gate_p, gate_bias_p, w_noise_p, noise_p, w_gate_s, gate_bias_s, w_noise_s, noise_s,
+                   topk_idx, topk_gate, counts_routed, aux_out=None, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_route_hier(ctypes.byref(p), _ptr(x), _ptr(w_gate_p), _ptr(gate_bias_p), _ptr(w_noise_p),
+                                _ptr(noise_p), _ptr(w_gate_s), _ptr(gate_bias_s), _ptr(w_noise_s), _ptr(noise_s),
+                                _ptr(topk_idx), _ptr(topk_gate), _ptr(counts_routed), _ptr(aux_out), wp, wn,
+                                _stream(stream)), "moe_route_hier")
+
+
+def moe_forward_hier(p, x, w_gate_p, gate_bias_p, w_noise_p, noise_p, w_gate_s, gate_bias_s, w_noise_s, noise_s,
+                     w1, w2, y, aux_out=None, topk_idx=None, topk_gate=None, counts_routed=None, counts_kept=None,
+                     slot_dest=None, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_forward_hier(ctypes.byref(p), _ptr(x), _ptr(w_gate_p), _ptr(gate_bias_p), _ptr(w_noise_p),
+                                  _ptr(noise_p), _ptr(w_gate_s), _ptr(gate_bias_s), _ptr(w_noise_s), _ptr(noise_s),
+                                  _ptr(w1), _ptr(w2), _ptr(y), _ptr(aux_out), _ptr(topk_idx), _ptr(topk_gate),
+                                  _ptr(counts_routed), _ptr(counts_kept), _ptr(slot_dest), wp, wn, _stream(stream)),
+           "moe_forward_hier")
+
+
+def moe_backward(p, x, w_gate, gate_bias, w_noise, noise, w1, w2, dy, loss_weights, dx, dw_gate, dgate_bias,
+                 dw_noise, dw1, dw2, dlogits=None, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    ws_, wi, wl = (float(v) for v in loss_weights)
+    _check(lib().moe_backward(ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(gate_bias), _ptr(w_noise), _ptr(noise),
+                              _ptr(w1), _ptr(w2), _ptr(dy), ws_, wi, wl, _ptr(dx), _ptr(dw_gate), _ptr(dgate_bias),
+                              _ptr(dw_noise), _ptr(dw1), _ptr(dw2), _ptr(dlogits), wp, wn, _stream(stream)),
+           "moe_backward")
 
 
 def moe_canonical_softplus(z, out, stream=None):

@@ -61,6 +61,28 @@ __device__ __forceinline__ float activation_bf16(float z) {
   }
 }
 
+// d act(z) / dz for the backward pass: ReLU -> 1 for z > 0, else 0; exact GELU
+// z Phi(z) -> Phi(z) + z phi(z), with Phi from the same erf approximation as
+// gelu_fast (|error| <= 1.5e-7) and phi(z) = exp(-z^2 / 2) / sqrt(2 pi).
+template <int ACT>
+__device__ __forceinline__ float activation_grad(float z) {
+  if constexpr (ACT == 0) {
+    return z > 0.0f ? 1.0f : 0.0f;
+  } else {
+    const float za = __builtin_amdgcn_fmed3f(fabsf(z), 0.0f, 10.0f);
+    const float a = za * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
+    float r = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+    r = __builtin_fmaf(r, t, 1.421413741f);
+    r = __builtin_fmaf(r, t, -0.284496736f);
+    r = __builtin_fmaf(r, t, 0.254829592f);
+    const float e = __builtin_amdgcn_exp2f(za * (za * (-0.5f * 1.4426950408889634f)));  // exp(-z^2 / 2)
+    const float q = r * t * e;                                                          // erfc(|z| / sqrt 2)
+    const float cdf = z >= 0.0f ? 1.0f - 0.5f * q : 0.5f * q;
+    return __builtin_fmaf(z * 0.3989422804014327f, e, cdf);
+  }
+}
+
 }  // namespace moe
 
 // ---------------------------------------------------------------------------
@@ -105,6 +127,7 @@ hipError_t launch_route_fused(const RouteLaunch& a, bool noisy, int force_fallba
 struct DispatchLaunch {
   int64_t T;
   int d, E, k, dtype;
+  int slot_major;  // drop order: 0 token order, 1 first-choice priority (walk slot-major)
   int64_t C;  // < 0: unlimited
   int64_t max_rows;
   const void* x;
@@ -168,3 +191,83 @@ struct CombineLaunch {
   void* y;
 };
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Backward pass
+// ---------------------------------------------------------------------------
+// The grouped products of the expert backward (bwd_gemm.hip).
+enum BwdGemmKind {
+  kBwdRecompute1,  // H1 = act(Xp W1[e]), D1 = act'(Xp W1[e])
+  kBwdRecompute2,  // O = H1 W2[e]
+  kBwdDataGrad2,   // dZ = (dO W2[e]^T) * D1
+  kBwdDataGrad1,   // dXp = dZ W1[e]^T
+  kBwdWeightGrad   // dW[e] = A[seg e]^T B[seg e]
+};
+struct BwdGemmArgs {
+  const uint16_t* A;  // element pointers (fp32 layers: float data behind the same pointers)
+  const uint16_t* B;
+  uint16_t* C;
+  uint16_t* C2;          // second output (kBwdRecompute1: act'(z))
+  const uint16_t* Dmul;  // elementwise factor of the output (kBwdDataGrad2)
+  const int32_t* offsets;
+  const int32_t* tile_start;  // M-tile map (segments on M)
+  int E, M, N, K, n_tiles_m, n_tiles_n;
+  int64_t lda, ldb, ldc;                      // row strides in elements
+  int64_t b_expert_stride, c_expert_stride;   // per-expert offsets of the weights / weight gradients
+  uint32_t a_bytes, b_bytes;                  // extents of the A buffer and (segments on K) the B buffer
+};
+int bwd_gemm_tile_rows(int dtype);
+int bwd_gemm_tile_cols(int dtype);
+hipError_t launch_bwd_gemm(BwdGemmKind kind, const BwdGemmArgs& g, int64_t blocks, int dtype, int act, hipStream_t s);
+// M-tile map of bm-row tiles over the expert segments (offsets [E+1] -> tile_start)
+hipError_t launch_tile_map(const int32_t* offsets, int E, int bm, int32_t* tile_start, hipStream_t s);
+
+struct BwdMiscArgs {
+  int64_t T;
+  int d, E, k, dtype, renormalize, noisy, lpad;
+  const void* x;
+  const void* w_gate;
+  const void* w_noise;
+  const float* noise;
+  const void* dy;
+  const void* o;   // [R, d] recomputed expert outputs
+  void* dO;        // [R, d] gate-scaled upstream rows
+  const int32_t* slot_dest;
+  const int32_t* topk_idx;
+  const float* topk_gate;
+  float* dg;       // [T, k] dL/dg from the combine
+  const double* red;  // the route's fp64 per-expert sums [3][E]
+  const int32_t* counts_routed;
+  double w_switch, w_imp, w_load;
+  float *dimp, *dload, *dpsw;  // [E] each
+  const float *H, *CL, *SG;    // canonical logits, clean logits, softplus [T][lpad]
+  float *dclean, *du;          // [T, E]
+  const void* dxp;             // [R, d]
+  void* dx;                    // [T, d]
+};
+hipError_t launch_bwd_gather(const BwdMiscArgs& b, hipStream_t s);
+hipError_t launch_bwd_gate(const BwdMiscArgs& b, hipStream_t s);
+int64_t bwd_gate_wgrad_chunks(int64_t T);
+hipError_t launch_bwd_gate_wgrad(const BwdMiscArgs& b, const float* G, float* dW, float* db, float* part,
+                                 float* part_b, hipStream_t s);
+hipError_t launch_bwd_dx(const BwdMiscArgs& b, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Hierarchical gate (route_hier.hip)
+// ---------------------------------------------------------------------------
+struct HierLaunch {
+  int64_t T;
+  int groups, per_group, k_group, k_expert, noisy_p, lpad_p, lpad_s;
+  const float *Hp, *CLp, *SGp;  // primary logits, clean logits, softplus [T][lpad_p]
+  const float* Hs;              // secondary logits [T][lpad_s], column g * per_group + j
+  int32_t* order_p;             // [T][k_group + 1] primary order (workspace)
+  float* gate_p;                // [T][k_group] primary gates (workspace)
+  int32_t* topk_idx;            // [T][k_group * k_expert]
+  float* topk_gate;
+  int32_t* counts_routed;       // [groups * per_group]
+  double* red;                  // [E + 2 groups]: combined importance, primary importance, primary load
+  float* aux_out;               // [3] or null
+};
+hipError_t launch_route_hier(const HierLaunch& h, hipStream_t s);
+hipError_t launch_route_logits(const RouteLaunch& a, hipStream_t s);
+int route_logit_pad(int E);

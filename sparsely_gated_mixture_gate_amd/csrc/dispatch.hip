@@ -8,6 +8,11 @@
 // walking tokens in order (slots in order within a token), each assignment
 // takes the next rank of its expert and is kept iff rank < C.
 //
+// Drop order: token order as above, or (option) first-choice priority, where every
+// token's first choice is ranked before any token's second choice ("moe paper
+// models" table 2, GShard row: top-2 with a capacity); the kernels then walk the
+// [T, k] tables slot-major, so ranks and rows follow (slot, token) order.
+//
 // Design (gfx950), up to four launches, all integer work exact and deterministic:
 //   count   per 1024-assignment block, per-expert counts (LDS integer atomics);
 //           in the forward path extra blocks also reduce the gate's per-block
@@ -32,6 +37,16 @@ namespace {
 
 constexpr int kChunk = 1024;  // assignments per block: 4 waves x 4 steps x 64 lanes
 
+// Walk position w -> index of the assignment in the [T, k] tables. Token order
+// (slot order within a token) walks the tables as stored; first-choice priority
+// walks slot 0 of every token, then slot 1, ...
+__device__ __forceinline__ int64_t walk_pos(int64_t w, const DispatchLaunch& a) {
+  return a.slot_major ? (w % a.T) * a.k + w / a.T : w;
+}
+__device__ __forceinline__ int64_t walk_token(int64_t w, const DispatchLaunch& a) {
+  return a.slot_major ? w % a.T : w / a.k;
+}
+
 // Blocks [0, nb): per-block expert histograms. Blocks past nb (forward path): the
 // routing step's per-expert sums, one expert per wave.
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx, int64_t n, int E,
@@ -50,7 +65,7 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   const int64_t base = (int64_t)blockIdx.x * kChunk;
   for (int i = threadIdx.x; i < kChunk; i += 256) {
     const int64_t a = base + i;
-    if (a < n) atomicAdd(&hist[idx[a]], 1);
+    if (a < n) atomicAdd(&hist[idx[walk_pos(a, tl)]], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) blk_cnt[(int64_t)e * nb + blockIdx.x] = hist[e];
@@ -231,9 +246,9 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
   int ex[4], loc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int64_t a = base + q * 64 + lane;
+    const int64_t a = base + q * 64 + lane;  // walk position
     const bool valid = a < n;
-    const int e = valid ? idx[a] : 0;
+    const int e = valid ? idx[walk_pos(a, so)] : 0;
     uint64_t same = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -260,8 +275,8 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
     for (int w = 0; w < wave; ++w) r += wcnt[w * E + e];
     const bool keep = C < 0 || r < C;
     const int32_t slot = keep ? (int32_t)((SCAN ? off_s[e] : offsets[e]) + r) : -1;
-    slot_dest[a] = slot;
-    if (keep) row_src[slot] = (int32_t)(a / k);
+    slot_dest[walk_pos(a, so)] = slot;
+    if (keep) row_src[slot] = (int32_t)walk_token(a, so);
     dropped[q] = !keep;
   }
   // top-1 layers: the output rows of dropped tokens are zero; the wave clears them
@@ -273,7 +288,7 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
       while (m) {
         const int j = __builtin_ctzll(m);
         m &= m - 1;
-        uint4* yr = y_zero + (base + q * 64 + j) * y_chunks;  // k = 1: assignment = token
+        uint4* yr = y_zero + (base + q * 64 + j) * y_chunks;  // k = 1: walk position = token
         for (int c = lane; c < y_chunks; c += 64) yr[c] = uint4{0u, 0u, 0u, 0u};
       }
     }

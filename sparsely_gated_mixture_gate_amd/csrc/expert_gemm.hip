@@ -269,8 +269,9 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
   };
 
   const int wm = wave / WN_W, wn = wave % WN_W;
-  // SKIP: 16-row MFMA tiles wholly past the segment are neither read nor multiplied
-  const int mact = SKIP ? __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - wm * WM + 15) / 16))) : MI;
+  // 16-row MFMA tiles wholly past the segment are neither read nor multiplied (SKIP
+  // shapes; and in the pipelined loop, the last, partial M-tile of each expert)
+  const int mact = (SKIP || PF) ? __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - wm * WM + 15) / 16))) : MI;
   const int g = lane >> 4;   // k-group of 8 inside a 32-wide k step
   const int s = lane & 15;
   floatx4 acc[MI][NI];
@@ -324,11 +325,14 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
     }
   };
 
-  if constexpr (PF) {
-    // Software pipeline over 32-wide k units: the operands of unit u + 1 are read
-    // from LDS into the second register set while the MFMAs of unit u run. A
-    // barrier precedes the first read of each k-tile; before it every wave has
-    // finished its reads of the previous k-tile, whose stage is then refilled.
+  // Software pipeline over 32-wide k units: the operands of unit u + 1 are read
+  // from LDS into the second register set while the MFMAs of unit u run. A
+  // barrier precedes the first read of each k-tile; before it every wave has
+  // finished its reads of the previous k-tile, whose stage is then refilled.
+  // DYN: this wave multiplies only its first mact 16-row tiles (a partial M-tile,
+  // or the SKIP shapes); full tiles keep a fixed, pinned instruction schedule.
+  auto pipelined = [&](auto dyn_c) {
+    constexpr bool DYN = decltype(dyn_c)::value;
     constexpr int KS = BK / 32;
     constexpr int Q = MI * NI;   // MFMAs per unit
     constexpr int NR = NI + MI;  // operand reads per unit (a B operand = two transposing reads)
@@ -340,18 +344,18 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         const int mi = q / NI, ni = q % NI;
-        if (!SKIP || mi < mact)
+        if (!DYN || mi < mact)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[CUR][ni], fa[CUR][mi], acc[mi][ni], 0, 0, 0);
-        if constexpr (!SKIP) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // this MFMA, then its reads
+        if constexpr (!DYN) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // this MFMA, then its reads
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           if ((r * Q) / NR != q) continue;
           if (r < NI) {
             fb[NXT][r] = rd_b(nst, nks, r);
-            if constexpr (!SKIP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          } else if (!SKIP || r - NI < mact) {
+            if constexpr (!DYN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          } else if (!DYN || r - NI < mact) {
             fa[NXT][r - NI] = rd_a(nst, nks, r - NI);
-            if constexpr (!SKIP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if constexpr (!DYN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
         }
       }
@@ -370,7 +374,7 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
     for (int ni = 0; ni < NI; ++ni) fb[0][ni] = rd_b(0, 0, ni);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
-      if (!SKIP || mi < mact) fa[0][mi] = rd_a(0, 0, mi);
+      if (!DYN || mi < mact) fa[0][mi] = rd_a(0, 0, mi);
     const int nu = nk * KS;
     // one unit: u = kt * KS + ks, register set u & 1
     auto step = [&](auto cur_c, int u) {
@@ -392,7 +396,12 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
       step(std::integral_constant<int, 0>{}, u);
       if (u + 1 < nu) step(std::integral_constant<int, 1>{}, u + 1);
     }
-  } else {
+  };
+  if constexpr (PF) {
+    if (SKIP || mact < MI) pipelined(std::true_type{});
+    else pipelined(std::false_type{});
+  }
+  if constexpr (!PF) {
 #pragma unroll
     for (int t = 0; t < NSTAGE - 1; ++t)
       if (t < nk) issue(t);
@@ -564,7 +573,7 @@ hipError_t launch_ffn_act(const FfnLaunch& a, hipStream_t s) {
     // layer 2 384 columns (two tiles of a 768-wide output)
     case kTiles160Skip: return launch_bf16<160, 32, 4, ACT, true, false, 8, 96, 384, 32, 3, 512, 128>(a, s);
     case kTiles256Skip: return launch_bf16<256, 32, 4, ACT, true, true>(a, s);
-    case kTiles256: return launch_bf16<256, 32, 4, ACT, false, true>(a, s);
+    case kTiles256: return launch_bf16<256, 32, 4, ACT, false, true, 8, 128>(a, s);
     // about one M-tile of rows per expert, no capacity: 256-column tiles on both layers
     // (twice the tiles of 512-column ones, so the tile rounds of a skewed routing stay
     // fuller: layer 2 of noisy_top4 has ~320 M-tiles for 256 CUs)
@@ -583,6 +592,11 @@ int ffn_tile_rows(int dtype, int64_t capacity, int64_t max_rows, int E) {
     case kTiles128: return 128;
     default: return 256;
   }
+}
+
+hipError_t launch_tile_map(const int32_t* offsets, int E, int bm, int32_t* tile_start, hipStream_t s) {
+  hipLaunchKernelGGL(moe::tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, tile_start);
+  return hipGetLastError();
 }
 
 hipError_t launch_expert_ffn(const FfnLaunch& a, hipStream_t s) {

@@ -70,6 +70,10 @@ moe_status check_params(const moe_params* p) {
   if (p->T * (int64_t)p->k >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*k = %lld >= 2^31", (long long)(p->T * p->k));
   if (isnan(p->capacity_factor)) return fail(MOE_ERR_INVALID_ARG, "capacity_factor is NaN");
+  if (p->drop_order != MOE_DROP_TOKEN_ORDER && p->drop_order != MOE_DROP_FIRST_CHOICE)
+    return fail(MOE_ERR_INVALID_ARG, "drop_order = %d (0 or 1)", p->drop_order);
+  if (p->groups < 0 || p->k_group < 0)
+    return fail(MOE_ERR_INVALID_ARG, "groups = %d and k_group = %d must be >= 0", p->groups, p->k_group);
   // 32-bit byte offsets inside one expert's weights and one row segment
   const int64_t elt = p->dtype == MOE_BF16 ? 2 : 4;
   const int64_t widest = p->d_model > p->d_ff ? p->d_model : p->d_ff;
@@ -79,6 +83,27 @@ moe_status check_params(const moe_params* p) {
   // 32-bit byte offsets inside the fp32 gate (+ noise) weights, column blocks of 128
   if ((int64_t)p->d_model * (2 * ((p->E + 63) / 64) * 64 + 128) * 4 >= (int64_t(1) << 31) - 16)
     return fail(MOE_ERR_UNSUPPORTED, "d_model * E too large for the gate weights' 32-bit byte offsets");
+  return MOE_OK;
+}
+
+// Hierarchical layers: groups g >= 1 dividing E (E / g experts per group), k_group
+// dividing k (k / k_group experts per kept group), k_group <= g, k / k_group <= E / g.
+moe_status check_hier(const moe_params* p) {
+  const int g = p->groups, kg = p->k_group;
+  if (g < 1 || kg < 1) return fail(MOE_ERR_INVALID_ARG, "hierarchical layer needs groups >= 1 and k_group >= 1");
+  if (p->E % g) return fail(MOE_ERR_INVALID_ARG, "E = %d is not a multiple of groups = %d", p->E, g);
+  if (p->k % kg) return fail(MOE_ERR_INVALID_ARG, "k = %d is not a multiple of k_group = %d", p->k, kg);
+  if (kg > g || p->k / kg > p->E / g)
+    return fail(MOE_ERR_INVALID_ARG, "k_group = %d > groups = %d or k / k_group = %d > E / groups = %d", kg, g,
+                p->k / kg, p->E / g);
+  return MOE_OK;
+}
+
+// The flat gate's entry points take flat layers only.
+moe_status check_flat(const moe_params* p) {
+  if (p->groups > 1)
+    return fail(MOE_ERR_INVALID_ARG, "groups = %d: a hierarchical layer's gate is moe_route_hier / moe_forward_hier",
+                p->groups);
   return MOE_OK;
 }
 
@@ -183,9 +208,82 @@ ForwardWs carve_forward(Carver& c, const moe_params* p, bool noisy) {
   return w;
 }
 
+struct HierWs {
+  float *wc_p, *lg_p, *wc_s, *lg_s;
+  int32_t* order_p;
+  float* gate_p;
+  double* red;
+};
+HierWs carve_route_hier(Carver& c, const moe_params* p, bool noisy_p, bool noisy_s) {
+  HierWs w;
+  const int g = p->groups > 0 ? p->groups : 1, kg = p->k_group > 0 ? p->k_group : 1;
+  const size_t T = (size_t)(p->T > 0 ? p->T : 1);
+  w.wc_p = c.take<float>(route_weight_floats(p->d_model, g, noisy_p));
+  w.lg_p = c.take<float>(route_logit_floats((int64_t)T, g, noisy_p));
+  w.wc_s = c.take<float>(route_weight_floats(p->d_model, p->E, noisy_s));
+  w.lg_s = c.take<float>(route_logit_floats((int64_t)T, p->E, noisy_s));
+  w.order_p = c.take<int32_t>(T * (size_t)(kg + 1));
+  w.gate_p = c.take<float>(T * (size_t)kg);
+  w.red = c.take<double>((size_t)p->E + 2 * (size_t)g);
+  return w;
+}
+
+struct ForwardHierWs {
+  HierWs route;
+  ForwardWs rest;  // its route part is unused
+};
+
+struct BackwardWs {
+  RouteWs route;  // the canonical gate keeps H, clean logits and softplus values in route.lg
+  int32_t* blk_cnt;
+  int32_t* tile_start;
+  int32_t *topk_idx, *counts_routed, *counts_kept, *offsets, *slot_dest, *row_src;
+  float *topk_gate, *dg, *dimp, *dload, *dpsw, *dclean, *du, *part, *part_b;
+  void *x_perm, *h1, *d1, *o, *dO;  // d1 holds act'(z), then dZ; o holds the outputs, then dXp
+};
+BackwardWs carve_backward(Carver& c, const moe_params* p, bool noisy) {
+  BackwardWs w;
+  const size_t tk = (size_t)(p->T * p->k > 0 ? p->T * p->k : 1);
+  const size_t rows = (size_t)(max_rows_of(p) > 0 ? max_rows_of(p) : 1);
+  const size_t te = (size_t)(p->T > 0 ? p->T : 1) * (size_t)p->E;
+  const size_t el = elt_size(p);
+  w.route = carve_route(c, p, noisy);
+  w.blk_cnt = carve_dispatch(c, p);
+  const int64_t bm = bwd_gemm_tile_rows(p->dtype);
+  w.tile_start = c.take<int32_t>((size_t)p->E + 1 + (size_t)((max_rows_of(p) + bm - 1) / bm + p->E));
+  w.topk_idx = c.take<int32_t>(tk);
+  w.counts_routed = c.take<int32_t>((size_t)p->E);
+  w.counts_kept = c.take<int32_t>((size_t)p->E);
+  w.offsets = c.take<int32_t>((size_t)p->E + 1);
+  w.slot_dest = c.take<int32_t>(tk);
+  w.row_src = c.take<int32_t>(rows);
+  w.topk_gate = c.take<float>(tk);
+  w.dg = c.take<float>(tk);
+  w.dimp = c.take<float>((size_t)p->E);
+  w.dload = c.take<float>((size_t)p->E);
+  w.dpsw = c.take<float>((size_t)p->E);
+  w.dclean = c.take<float>(te);
+  w.du = noisy ? c.take<float>(te) : nullptr;
+  const int64_t nc = bwd_gate_wgrad_chunks(p->T);
+  w.part = c.take<float>((size_t)(nc > 0 ? nc : 1) * (size_t)p->d_model * (size_t)p->E);
+  w.part_b = c.take<float>((size_t)(nc > 0 ? nc : 1) * (size_t)p->E);
+  w.x_perm = c.take<char>(rows * (size_t)p->d_model * el);
+  w.h1 = c.take<char>(rows * (size_t)p->d_ff * el);
+  w.d1 = c.take<char>(rows * (size_t)p->d_ff * el);
+  w.o = c.take<char>(rows * (size_t)p->d_model * el);
+  w.dO = c.take<char>(rows * (size_t)p->d_model * el);
+  return w;
+}
+
 size_t ws_bytes_for(const moe_params* p, int op, bool noisy) {
   Carver c(nullptr);
   switch (op) {
+    case MOE_OP_BACKWARD: carve_backward(c, p, noisy); break;
+    case MOE_OP_ROUTE_HIER: carve_route_hier(c, p, true, true); break;
+    case MOE_OP_FORWARD_HIER:
+      carve_route_hier(c, p, true, true);
+      carve_forward(c, p, false);
+      break;
     case MOE_OP_ROUTE: carve_route(c, p, noisy); break;
     case MOE_OP_DISPATCH: carve_dispatch(c, p); break;
     case MOE_OP_EXPERT_FFN: carve_ffn(c, p); break;
@@ -267,6 +365,7 @@ moe_status run_dispatch(const moe_params* p, const void* x, const int32_t* topk_
   a.E = p->E;
   a.k = p->k;
   a.dtype = p->dtype;
+  a.slot_major = p->drop_order == MOE_DROP_FIRST_CHOICE && p->k > 1 ? 1 : 0;
   a.C = capacity_of(p);
   a.max_rows = max_rows_of(p);
   a.x = x;
@@ -379,6 +478,93 @@ moe_status check_dispatch_args(const moe_params* p, const void* x, const int32_t
   return MOE_OK;
 }
 
+// Everything of the forward after the gate: dispatch (with the route's tail when
+// route_tail is given), expert FFN, combine. bf16: the expert GEMM gathers its rows
+// from x (no x_perm copy); top-1 layers also write the gated expert outputs
+// straight into y (no combine pass; the dispatch zeroes the rows of dropped tokens).
+moe_status forward_tail(const moe_params* p, const void* x, const void* w1, const void* w2, void* y, float* aux_out,
+                        int32_t* idx, float* gate, int32_t* cr, int32_t* ck, int32_t* sd, const ForwardWs& w,
+                        const RouteWs* route_tail, bool noisy, hipStream_t s) {
+  moe_status st;
+  hipError_t he;
+  const bool fused = p->dtype == MOE_BF16;
+  const bool direct_y = fused && p->k == 1;
+  if ((st = run_dispatch(p, x, idx, ck, w.offsets, sd, w.row_src, w.x_perm, w.blk_cnt, w.ffn.tile_start, fused,
+                         direct_y ? y : nullptr, s, route_tail, cr, aux_out, noisy)) != MOE_OK)
+    return st;
+  if ((he = record_phase(2, s)) != hipSuccess) return hip_fail(he, "phase event");
+  if ((st = run_ffn(p, w.x_perm, w.offsets, w1, w2, w.y_perm, w.ffn, true, s, fused ? x : nullptr,
+                    fused ? w.row_src : nullptr, direct_y ? y : nullptr, direct_y ? gate : nullptr,
+                    g_phase_ev[3])) != MOE_OK)
+    return st;
+  if ((he = record_phase(4, s)) != hipSuccess) return hip_fail(he, "phase event");
+  if (!direct_y && (st = run_combine(p, w.y_perm, sd, gate, y, s)) != MOE_OK) return st;
+  if ((he = record_phase(5, s)) != hipSuccess) return hip_fail(he, "phase event");
+  return MOE_OK;
+}
+
+// The hierarchical gate: both gates' canonical logits, selection, sums, losses.
+moe_status run_route_hier(const moe_params* p, const void* x, const void* w_gate_p, const float* gate_bias_p,
+                          const void* w_noise_p, const float* noise_p, const void* w_gate_s, const float* gate_bias_s,
+                          const void* w_noise_s, const float* noise_s, int32_t* topk_idx, float* topk_gate,
+                          int32_t* counts_routed, float* aux_out, const HierWs& w, hipStream_t s) {
+  auto logits = [&](int E, const void* wg, const float* b, const void* wn, const float* eps, float* wc, float* lg) {
+    RouteLaunch a{};
+    a.T = p->T;
+    a.d = p->d_model;
+    a.E = E;
+    a.k = 1;
+    a.dtype = p->dtype;
+    a.x = x;
+    a.w_gate = wg;
+    a.gate_bias = b;
+    a.w_noise = wn;
+    a.noise = eps;
+    a.wc = wc;
+    a.lg = lg;
+    return launch_route_logits(a, s);
+  };
+  hipError_t he = logits(p->groups, w_gate_p, gate_bias_p, w_noise_p, noise_p, w.wc_p, w.lg_p);
+  if (he != hipSuccess) return hip_fail(he, "primary gate launch");
+  if ((he = logits(p->E, w_gate_s, gate_bias_s, w_noise_s, noise_s, w.wc_s, w.lg_s)) != hipSuccess)
+    return hip_fail(he, "secondary gate launch");
+  HierLaunch h{};
+  h.T = p->T;
+  h.groups = p->groups;
+  h.per_group = p->E / p->groups;
+  h.k_group = p->k_group;
+  h.k_expert = p->k / p->k_group;
+  h.noisy_p = w_noise_p != nullptr;
+  h.lpad_p = route_logit_pad(p->groups);
+  h.lpad_s = route_logit_pad(p->E);
+  const size_t np = (size_t)(p->T > 0 ? p->T : 0) * (size_t)h.lpad_p;
+  h.Hp = w.lg_p;
+  h.CLp = w_noise_p ? w.lg_p + np : nullptr;
+  h.SGp = w_noise_p ? w.lg_p + 2 * np : nullptr;
+  h.Hs = w.lg_s;
+  h.order_p = w.order_p;
+  h.gate_p = w.gate_p;
+  h.topk_idx = topk_idx;
+  h.topk_gate = topk_gate;
+  h.counts_routed = counts_routed;
+  h.red = w.red;
+  h.aux_out = aux_out;
+  he = launch_route_hier(h, s);
+  return he == hipSuccess ? MOE_OK : hip_fail(he, "hierarchical gate launch");
+}
+
+moe_status check_hier_inputs(const moe_params* p, const void* x, const void* w_gate_p, const void* w_noise_p,
+                             const float* noise_p, const void* w_gate_s, const void* w_noise_s, const float* noise_s) {
+  moe_status st = check_hier(p);
+  if (st != MOE_OK) return st;
+  if (p->T > 0) REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(w_gate_p, "w_gate_p");
+  REQUIRE_PTR(w_gate_s, "w_gate_s");
+  if ((w_noise_p == nullptr) != (noise_p == nullptr) || (w_noise_s == nullptr) != (noise_s == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "each level's w_noise and noise must both be given or both be NULL");
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -410,7 +596,8 @@ moe_status moe_workspace_size(const moe_params* p, int op, size_t* bytes) {
   moe_status st = check_params(p);
   if (st != MOE_OK) return st;
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-  if (op < MOE_OP_ROUTE || op > MOE_OP_FORWARD) return fail(MOE_ERR_INVALID_ARG, "op = %d", op);
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FORWARD_HIER) return fail(MOE_ERR_INVALID_ARG, "op = %d", op);
+  if ((op == MOE_OP_ROUTE_HIER || op == MOE_OP_FORWARD_HIER) && (st = check_hier(p)) != MOE_OK) return st;
   // The noisy gate uses no extra workspace; size for it either way.
   *bytes = ws_bytes_for(p, op, true);
   return MOE_OK;
@@ -422,6 +609,7 @@ moe_status moe_route(const moe_params* p, const void* x, const void* w_gate, con
                      void* stream) {
   moe_status st = check_params(p);
   if (st != MOE_OK) return st;
+  if ((st = check_flat(p)) != MOE_OK) return st;
   if ((st = check_route_inputs(p, x, w_gate, w_noise, noise)) != MOE_OK) return st;
   if (p->T > 0) {
     REQUIRE_PTR(topk_idx, "topk_idx");
@@ -503,6 +691,7 @@ moe_status moe_forward(const moe_params* p, const void* x, const void* w_gate, c
                        int32_t* counts_kept, int32_t* slot_dest, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_params(p);
   if (st != MOE_OK) return st;
+  if ((st = check_flat(p)) != MOE_OK) return st;
   if ((st = check_route_inputs(p, x, w_gate, w_noise, noise)) != MOE_OK) return st;
   REQUIRE_PTR(w1, "w1");
   REQUIRE_PTR(w2, "w2");
@@ -527,23 +716,216 @@ moe_status moe_forward(const moe_params* p, const void* x, const void* w_gate, c
       MOE_OK)
     return st;
   if ((he = record_phase(1, s)) != hipSuccess) return hip_fail(he, "phase event");
-  // bf16: the expert GEMM gathers its rows from x (no x_perm copy); top-1 layers also
-  // write the gated expert outputs straight into y (no combine pass; the dispatch
-  // zeroes the rows of dropped tokens)
-  const bool fused = p->dtype == MOE_BF16;
-  const bool direct_y = fused && p->k == 1;
-  if ((st = run_dispatch(p, x, idx, ck, w.offsets, sd, w.row_src, w.x_perm, w.blk_cnt, w.ffn.tile_start, fused,
-                         direct_y ? y : nullptr, s, &w.route, cr, aux_out, noisy)) != MOE_OK)
+  return forward_tail(p, x, w1, w2, y, aux_out, idx, gate, cr, ck, sd, w, &w.route, noisy, s);
+}
+
+moe_status moe_backward(const moe_params* p, const void* x, const void* w_gate, const float* gate_bias,
+                        const void* w_noise, const float* noise, const void* w1, const void* w2, const void* dy,
+                        double w_switch, double w_importance, double w_load, void* dx, float* dw_gate,
+                        float* dgate_bias, float* dw_noise, void* dw1, void* dw2, float* dlogits, void* ws,
+                        size_t ws_bytes, void* stream) {
+  moe_status st = check_params(p);
+  if (st != MOE_OK) return st;
+  if ((st = check_flat(p)) != MOE_OK) return st;
+  if ((st = check_route_inputs(p, x, w_gate, w_noise, noise)) != MOE_OK) return st;
+  REQUIRE_PTR(w1, "w1");
+  REQUIRE_PTR(w2, "w2");
+  REQUIRE_PTR(dw_gate, "dw_gate");
+  REQUIRE_PTR(dw1, "dw1");
+  REQUIRE_PTR(dw2, "dw2");
+  if (p->T > 0) {
+    REQUIRE_PTR(dy, "dy");
+    REQUIRE_PTR(dx, "dx");
+  }
+  const bool noisy = w_noise != nullptr;
+  if (noisy) REQUIRE_PTR(dw_noise, "dw_noise");
+  if (dgate_bias && !aligned16(dgate_bias)) return fail(MOE_ERR_INVALID_ARG, "dgate_bias is not 16-byte aligned");
+  if (dlogits && !aligned16(dlogits)) return fail(MOE_ERR_INVALID_ARG, "dlogits is not 16-byte aligned");
+  if (!(isfinite(w_switch) && isfinite(w_importance) && isfinite(w_load)))
+    return fail(MOE_ERR_INVALID_ARG, "loss weights must be finite");
+  if ((st = check_ws(p, MOE_OP_BACKWARD, noisy, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c(ws);
+  const BackwardWs w = carve_backward(c, p, noisy);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the gate on its canonical fp32 path, which keeps H, the clean logits and the
+  // softplus values; the same routing as the forward in every gate mode
+  moe_params pc = *p;
+  pc.gate_mode = MOE_GATE_CANONICAL;
+  if ((st = run_route(&pc, x, w_gate, gate_bias, w_noise, noise, w.topk_idx, w.topk_gate, w.counts_routed, nullptr,
+                      nullptr, w.route, s)) != MOE_OK)
     return st;
-  if ((he = record_phase(2, s)) != hipSuccess) return hip_fail(he, "phase event");
-  if ((st = run_ffn(p, w.x_perm, w.offsets, w1, w2, w.y_perm, w.ffn, true, s, fused ? x : nullptr,
-                    fused ? w.row_src : nullptr, direct_y ? y : nullptr, direct_y ? gate : nullptr,
-                    g_phase_ev[3])) != MOE_OK)
+  if ((st = run_dispatch(p, x, w.topk_idx, w.counts_kept, w.offsets, w.slot_dest, w.row_src, w.x_perm, w.blk_cnt,
+                         nullptr, false, nullptr, s)) != MOE_OK)
     return st;
-  if ((he = record_phase(4, s)) != hipSuccess) return hip_fail(he, "phase event");
-  if (!direct_y && (st = run_combine(p, w.y_perm, sd, gate, y, s)) != MOE_OK) return st;
-  if ((he = record_phase(5, s)) != hipSuccess) return hip_fail(he, "phase event");
+  const int bm = bwd_gemm_tile_rows(p->dtype), bn = bwd_gemm_tile_cols(p->dtype);
+  hipError_t he = launch_tile_map(w.offsets, p->E, bm, w.tile_start, s);
+  if (he != hipSuccess) return hip_fail(he, "tile map launch");
+  const int64_t R = max_rows_of(p);
+  const int d = p->d_model, f = p->d_ff;
+  const uint32_t el = (uint32_t)elt_size(p);
+  const int64_t mtiles = (R + bm - 1) / bm + p->E;
+  auto seg_m = [&](const void* A, int64_t lda, const void* B, int64_t ldb, void* C, void* C2, const void* Dm,
+                   int N, int K) {
+    BwdGemmArgs g{};
+    g.A = static_cast<const uint16_t*>(A);
+    g.B = static_cast<const uint16_t*>(B);
+    g.C = static_cast<uint16_t*>(C);
+    g.C2 = static_cast<uint16_t*>(C2);
+    g.Dmul = static_cast<const uint16_t*>(Dm);
+    g.offsets = w.offsets;
+    g.tile_start = w.tile_start;
+    g.E = p->E;
+    g.N = N;
+    g.K = K;
+    g.n_tiles_n = (N + bn - 1) / bn;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.ldc = N;
+    g.b_expert_stride = (int64_t)d * f;
+    g.a_bytes = (uint32_t)(R * lda * el);
+    return g;
+  };
+  auto run = [&](BwdGemmKind kind, const BwdGemmArgs& g, int64_t blocks, const char* what) -> moe_status {
+    const hipError_t e = launch_bwd_gemm(kind, g, blocks, p->dtype, p->act, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, what);
+  };
+  // recompute the expert FFN: H1 = act(Xp W1), D1 = act'(Xp W1), O = H1 W2
+  BwdGemmArgs g = seg_m(w.x_perm, d, w1, f, w.h1, w.d1, nullptr, f, d);
+  if ((st = run(kBwdRecompute1, g, mtiles * g.n_tiles_n, "expert backward launch")) != MOE_OK) return st;
+  g = seg_m(w.h1, f, w2, d, w.o, nullptr, nullptr, d, f);
+  if ((st = run(kBwdRecompute2, g, mtiles * g.n_tiles_n, "expert backward launch")) != MOE_OK) return st;
+  // combine adjoint (dO = g dy), dL/dg, and the gate's backward
+  BwdMiscArgs b{};
+  b.T = p->T;
+  b.d = d;
+  b.E = p->E;
+  b.k = p->k;
+  b.dtype = p->dtype;
+  b.renormalize = p->renormalize;
+  b.noisy = noisy ? 1 : 0;
+  b.lpad = (p->E + 3) & ~3;
+  b.x = x;
+  b.w_gate = w_gate;
+  b.w_noise = w_noise;
+  b.noise = noise;
+  b.dy = dy;
+  b.o = w.o;
+  b.dO = w.dO;
+  b.slot_dest = w.slot_dest;
+  b.topk_idx = w.topk_idx;
+  b.topk_gate = w.topk_gate;
+  b.dg = w.dg;
+  b.red = w.route.red;
+  b.counts_routed = w.counts_routed;
+  b.w_switch = w_switch;
+  b.w_imp = w_importance;
+  b.w_load = w_load;
+  b.dimp = w.dimp;
+  b.dload = w.dload;
+  b.dpsw = w.dpsw;
+  const size_t lpn = (size_t)(p->T > 0 ? p->T : 0) * (size_t)b.lpad;
+  b.H = w.route.lg;
+  b.CL = noisy ? w.route.lg + lpn : nullptr;
+  b.SG = noisy ? w.route.lg + 2 * lpn : nullptr;
+  b.dclean = dlogits ? dlogits : w.dclean;
+  b.du = w.du;
+  b.dxp = w.o;
+  b.dx = dx;
+  if ((he = launch_bwd_gather(b, s)) != hipSuccess) return hip_fail(he, "backward gather launch");
+  if ((he = launch_bwd_gate(b, s)) != hipSuccess) return hip_fail(he, "gate backward launch");
+  // data gradients: dZ = (dO W2^T) * act'(z) (in place over D1), dXp = dZ W1^T (over O)
+  g = seg_m(w.dO, d, w2, d, w.d1, nullptr, w.d1, f, d);
+  if ((st = run(kBwdDataGrad2, g, mtiles * g.n_tiles_n, "expert backward launch")) != MOE_OK) return st;
+  g = seg_m(w.d1, f, w1, f, w.o, nullptr, nullptr, d, f);
+  if ((st = run(kBwdDataGrad1, g, mtiles * g.n_tiles_n, "expert backward launch")) != MOE_OK) return st;
+  // weight gradients over each expert's rows: dW2 = H1^T dO, dW1 = Xp^T dZ
+  auto seg_k = [&](const void* A, int M, const void* B, int N, void* C) {
+    BwdGemmArgs q{};
+    q.A = static_cast<const uint16_t*>(A);
+    q.B = static_cast<const uint16_t*>(B);
+    q.C = static_cast<uint16_t*>(C);
+    q.offsets = w.offsets;
+    q.E = p->E;
+    q.M = M;
+    q.N = N;
+    q.n_tiles_m = (M + bm - 1) / bm;
+    q.n_tiles_n = (N + bn - 1) / bn;
+    q.lda = M;
+    q.ldb = N;
+    q.ldc = N;
+    q.c_expert_stride = (int64_t)M * N;
+    q.a_bytes = (uint32_t)(R * M * el);
+    q.b_bytes = (uint32_t)(R * N * el);
+    return q;
+  };
+  g = seg_k(w.h1, f, w.dO, d, dw2);
+  if ((st = run(kBwdWeightGrad, g, (int64_t)p->E * g.n_tiles_m * g.n_tiles_n, "weight gradient launch")) != MOE_OK)
+    return st;
+  g = seg_k(w.x_perm, d, w.d1, f, dw1);
+  if ((st = run(kBwdWeightGrad, g, (int64_t)p->E * g.n_tiles_m * g.n_tiles_n, "weight gradient launch")) != MOE_OK)
+    return st;
+  // gate weight gradients and dx
+  if ((he = launch_bwd_gate_wgrad(b, b.dclean, dw_gate, gate_bias ? dgate_bias : nullptr, w.part, w.part_b, s)) !=
+      hipSuccess)
+    return hip_fail(he, "gate weight gradient launch");
+  if (noisy && (he = launch_bwd_gate_wgrad(b, w.du, dw_noise, nullptr, w.part, w.part_b, s)) != hipSuccess)
+    return hip_fail(he, "noise weight gradient launch");
+  if ((he = launch_bwd_dx(b, s)) != hipSuccess) return hip_fail(he, "dx launch");
   return MOE_OK;
+}
+
+moe_status moe_route_hier(const moe_params* p, const void* x, const void* w_gate_p, const float* gate_bias_p,
+                          const void* w_noise_p, const float* noise_p, const void* w_gate_s, const float* gate_bias_s,
+                          const void* w_noise_s, const float* noise_s, int32_t* topk_idx, float* topk_gate,
+                          int32_t* counts_routed, float* aux_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_params(p);
+  if (st != MOE_OK) return st;
+  if ((st = check_hier_inputs(p, x, w_gate_p, w_noise_p, noise_p, w_gate_s, w_noise_s, noise_s)) != MOE_OK) return st;
+  if (p->T > 0) {
+    REQUIRE_PTR(topk_idx, "topk_idx");
+    REQUIRE_PTR(topk_gate, "topk_gate");
+  }
+  REQUIRE_PTR(counts_routed, "counts_routed");
+  if (aux_out && !aligned16(aux_out)) return fail(MOE_ERR_INVALID_ARG, "aux_out is not 16-byte aligned");
+  if ((st = check_ws(p, MOE_OP_ROUTE_HIER, true, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c(ws);
+  const HierWs w = carve_route_hier(c, p, true, true);
+  return run_route_hier(p, x, w_gate_p, gate_bias_p, w_noise_p, noise_p, w_gate_s, gate_bias_s, w_noise_s, noise_s,
+                        topk_idx, topk_gate, counts_routed, aux_out, w, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_forward_hier(const moe_params* p, const void* x, const void* w_gate_p, const float* gate_bias_p,
+                            const void* w_noise_p, const float* noise_p, const void* w_gate_s,
+                            const float* gate_bias_s, const void* w_noise_s, const float* noise_s, const void* w1,
+                            const void* w2, void* y, float* aux_out, int32_t* topk_idx, float* topk_gate,
+                            int32_t* counts_routed, int32_t* counts_kept, int32_t* slot_dest, void* ws,
+                            size_t ws_bytes, void* stream) {
+  moe_status st = check_params(p);
+  if (st != MOE_OK) return st;
+  if ((st = check_hier_inputs(p, x, w_gate_p, w_noise_p, noise_p, w_gate_s, w_noise_s, noise_s)) != MOE_OK) return st;
+  REQUIRE_PTR(w1, "w1");
+  REQUIRE_PTR(w2, "w2");
+  if (p->T > 0) REQUIRE_PTR(y, "y");
+  const void* opt[] = {aux_out, topk_idx, topk_gate, counts_routed, counts_kept, slot_dest};
+  for (const void* q : opt)
+    if (q && !aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "an optional output is not 16-byte aligned");
+  if ((st = check_ws(p, MOE_OP_FORWARD_HIER, true, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c(ws);
+  const HierWs wr = carve_route_hier(c, p, true, true);
+  const ForwardWs w = carve_forward(c, p, false);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* idx = topk_idx ? topk_idx : w.topk_idx;
+  float* gate = topk_gate ? topk_gate : w.topk_gate;
+  int32_t* cr = counts_routed ? counts_routed : w.counts_routed;
+  int32_t* ck = counts_kept ? counts_kept : w.counts_kept;
+  int32_t* sd = slot_dest ? slot_dest : w.slot_dest;
+  hipError_t he;
+  if ((he = record_phase(0, s)) != hipSuccess) return hip_fail(he, "phase event");
+  if ((st = run_route_hier(p, x, w_gate_p, gate_bias_p, w_noise_p, noise_p, w_gate_s, gate_bias_s, w_noise_s, noise_s,
+                           idx, gate, cr, aux_out, wr, s)) != MOE_OK)
+    return st;
+  if ((he = record_phase(1, s)) != hipSuccess) return hip_fail(he, "phase event");
+  return forward_tail(p, x, w1, w2, y, nullptr, idx, gate, cr, ck, sd, w, nullptr, false, s);
 }
 
 // Phase events of moe_forward on the calling thread (n = 0 or events NULL: off).

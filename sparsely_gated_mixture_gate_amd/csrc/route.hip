@@ -671,6 +671,17 @@ hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
   return err;
 }
 
+// Canonical logits only (H, and for the noisy gate the clean logits and softplus
+// values) into a.lg, [T][lpad] each, using a.wc for the widened weights.
+hipError_t launch_route_logits(const RouteLaunch& a, hipStream_t s) {
+  using namespace moe;
+  if (a.T <= 0) return hipSuccess;
+  const bool noisy = a.w_noise != nullptr;
+  return a.dtype == 1 ? launch_logits<uint16_t>(a, noisy, s) : launch_logits<float>(a, noisy, s);
+}
+
+int route_logit_pad(int E) { return moe::route_lpad(E); }
+
 hipError_t launch_softplus(const float* z, float* out, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(moe::softplus_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, z, out, n);

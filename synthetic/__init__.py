@@ -13,3 +13,4 @@ from .generate import (  # noqa: F401
     make_inputs,
     zipf_gate_bias,
 )
+from .hier import HIER_CONFIGS, HierConfig, hier_scaled, make_hier_inputs  # noqa: F401

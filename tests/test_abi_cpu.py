@@ -49,7 +49,7 @@ def test_capacity_and_row_bound(moelib):
 
 
 def test_workspace_sizes(moelib):
-    for op in range(4):
+    for op in range(5):
         small = moelib.moe_workspace_size(_p(moelib, T=100), op)
         big = moelib.moe_workspace_size(_p(moelib, T=10000), op)
         assert 0 < small <= big and small % 256 == 0
@@ -57,6 +57,8 @@ def test_workspace_sizes(moelib):
     assert fwd >= sum(moelib.moe_workspace_size(_p(moelib), op) for op in range(3))
     # the expert FFN workspace holds the bf16 hidden activations of every row
     assert moelib.moe_workspace_size(_p(moelib), moelib.MOE_OP_EXPERT_FFN) >= 2000 * 128 * 2
+    # the backward keeps the permuted rows, both hidden tensors, outputs and upstream rows
+    assert moelib.moe_workspace_size(_p(moelib), moelib.MOE_OP_BACKWARD) >= 2000 * (2 * 64 + 2 * 128 + 64) * 2
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -71,6 +73,8 @@ def test_workspace_sizes(moelib):
     (dict(T=2**30, k=2), "MOE_ERR_UNSUPPORTED"),
     (dict(gate_mode=3), "MOE_ERR_INVALID_ARG"),
     (dict(gate_mode=-1), "MOE_ERR_INVALID_ARG"),
+    (dict(drop_order=2), "MOE_ERR_INVALID_ARG"),
+    (dict(drop_order=-1), "MOE_ERR_INVALID_ARG"),
 ])
 def test_invalid_params_rejected(moelib, kw, status):
     with pytest.raises(moelib.MoEError) as ei:
@@ -105,3 +109,23 @@ def test_entry_points_validate_before_launch(moelib):
     with pytest.raises(moelib.MoEError) as ei:
         moelib.moe_forward(p, fake, fake, None, None, None, fake, fake, None, stream=0)
     assert "y is NULL" in str(ei.value)
+
+
+def test_backward_validates_before_launch(moelib):
+    p = _p(moelib)
+    fake = 1 << 20
+    args = dict(x=fake, w_gate=fake, gate_bias=None, w_noise=None, noise=None, w1=fake, w2=fake, dy=fake,
+                loss_weights=(0.0, 0.0, 0.0), dx=fake, dw_gate=fake, dgate_bias=None, dw_noise=None, dw1=fake,
+                dw2=fake, dlogits=None, ws=None, stream=0)
+    with pytest.raises(moelib.MoEError) as ei:  # no workspace
+        moelib.moe_backward(p, **args)
+    assert ei.value.status == moelib.MOE_ERR_WORKSPACE
+    with pytest.raises(moelib.MoEError) as ei:
+        moelib.moe_backward(p, **{**args, "dw1": None})
+    assert "dw1 is NULL" in str(ei.value)
+    with pytest.raises(moelib.MoEError) as ei:  # noisy gate without dw_noise
+        moelib.moe_backward(p, **{**args, "w_noise": fake, "noise": fake})
+    assert "dw_noise" in str(ei.value)
+    with pytest.raises(moelib.MoEError) as ei:
+        moelib.moe_backward(p, **{**args, "loss_weights": (float("nan"), 0.0, 0.0)})
+    assert "finite" in str(ei.value)

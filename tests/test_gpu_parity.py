@@ -3,8 +3,11 @@ same seeded inputs.
 
 Full-size cases run the five layer workloads at their real shapes in the
 launch configuration the benchmark times; the oracle checks all integer
-outputs and the gate logits exactly, and the expert FFN / combine / layer
-output on sampled rows (segment edges + random rows) or sampled tokens.
+outputs and the gate logits exactly, the layer output on every token of the
+three smaller workloads and, on the two largest, on 1024 random tokens plus
+every dropped token and the tokens at every expert segment's edges, and the
+expert FFN on segment edges plus random rows. Over the whole output, every
+row must be finite and fully dropped tokens' rows exactly zero.
 Small cases cover ragged and degenerate shapes element by element.
 """
 
@@ -43,15 +46,16 @@ def _case(name, **over):
 
     base = CONFIGS[name]
     cap = over.pop("capacity", -1)
+    first_choice = bool(over.pop("first_choice", False))
     cfg = scaled(base, **over) if over else base
     say(f"[case] generating {cfg.name}")
     inp = make_inputs(cfg)
-    spec = oracle.LayerSpec.of(cfg, capacity=cap)
+    spec = oracle.LayerSpec.of(cfg, capacity=cap, slot_major=first_choice)
     r = oracle.route(spec, inp)
     C = oracle.capacity(cfg.T, cfg.E, cfg.k, cfg.capacity_factor, cap)
-    disp = oracle.dispatch(r["topk_idx"], cfg.E, C)
+    disp = oracle.dispatch(r["topk_idx"], cfg.E, C, slot_major=first_choice)
     d_inp = {k_: to_device(v) for k_, v in inp.items()}
-    out = dict(cfg=cfg, spec=spec, inp=inp, route=r, C=C, disp=disp, dev=d_inp, cap=cap)
+    out = dict(cfg=cfg, spec=spec, inp=inp, route=r, C=C, disp=disp, dev=d_inp, cap=cap, first_choice=first_choice)
     _CACHE[key] = out
     return out
 
@@ -59,7 +63,7 @@ def _case(name, **over):
 def _params(moelib, c, gate_mode=0):
     cfg = c["cfg"]
     return moelib.make_params(cfg.T, cfg.d_model, cfg.d_ff, cfg.E, cfg.k, cfg.dtype, cfg.act, cfg.renormalize,
-                              cfg.capacity_factor, c["cap"], gate_mode)
+                              cfg.capacity_factor, c["cap"], gate_mode, int(c.get("first_choice", False)))
 
 
 def test_canonical_softplus_bitwise(moelib, dev):
@@ -232,16 +236,70 @@ def _check_forward(c, fb, tokens):
     rel_rows_ok(got, ref["y"], TOL[cfg.dtype], f"y {cfg.name}")
 
 
+# workloads whose every token the oracle evaluates in seconds; the larger two check
+# 1024 random tokens, every dropped token and the first / last token of every
+# expert segment (the ragged edges of the GEMM tiles)
+ALL_TOKENS = {"tiny_fp32", "switch_top1", "noisy_top4"}
+
+
+def _forward_tokens(c):
+    cfg, disp = c["cfg"], c["disp"]
+    if cfg.name in ALL_TOKENS:
+        return np.arange(cfg.T)
+    rng = np.random.default_rng(2)
+    dropped = np.flatnonzero((disp["slot_dest"] < 0).any(axis=1))
+    edges = disp["row_src"][sample_rows(disp["offsets"], 0)] if disp["R"] else np.zeros(0, np.int64)
+    return np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 1024), dropped, edges]))
+
+
+def _check_whole_y(c, fb):
+    """Over the whole output: every row finite (the NaN pre-fill is gone) and the
+    row of every token whose slots were all dropped exactly zero."""
+    import torch
+
+    cfg, disp = c["cfg"], c["disp"]
+    assert bool(torch.isfinite(fb.y).all()), "y has non-finite entries (a row was not written?)"
+    dead = np.flatnonzero((disp["slot_dest"] < 0).all(axis=1))
+    if dead.size:
+        rows = fb.y[torch.from_numpy(dead).to(fb.y.device)]
+        assert bool((rows == 0).all()), "a fully dropped token's row is not zero"
+    say(f"  whole y finite; {dead.size} fully dropped rows are zero")
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_forward_full_size(moelib, dev, name):
     c = _case(name)
     cfg = c["cfg"]
     say(f"[forward] {cfg.name}")
     fb = _run_forward(moelib, c, dev)
-    rng = np.random.default_rng(2)
-    n = cfg.T if cfg.T * cfg.d_model * cfg.d_ff <= 2**26 else 48
-    tokens = np.arange(cfg.T) if n == cfg.T else np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, n)]))
+    _check_whole_y(c, fb)
+    tokens = _forward_tokens(c)
+    say(f"  comparing {tokens.size} of {cfg.T} tokens with the oracle")
     _check_forward(c, fb, tokens)
+
+
+@pytest.mark.parametrize("cap", [-1, 1024])
+def test_forward_first_choice_full_size(moelib, dev, cap):
+    """The top-2 workload with first-choice priority, at the capacity factor's
+    C = 2048 and at C = 1024 (the T * cf / E reading, which drops ~4%)."""
+    c = _case("gshard_top2", first_choice=True, capacity=cap)
+    say(f"[forward-first-choice] C={c['C']} drops={int((c['disp']['slot_dest'] < 0).sum())}")
+    fb = _run_forward(moelib, c, dev)
+    _check_whole_y(c, fb)
+    _check_forward(c, fb, _forward_tokens(c))
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size_is_deterministic(moelib, dev, name):
+    """Two forwards of the same inputs give the same bytes in every output."""
+    from sparsely_gated_mixture_gate_amd.buffers import to_numpy
+
+    c = _case(name)
+    say(f"[determinism] {c['cfg'].name} x2")
+    a = _run_forward(moelib, c, dev)
+    b = _run_forward(moelib, c, dev)
+    for f in ("y", "aux", "topk_idx", "topk_gate", "counts_routed", "counts_kept", "slot_dest"):
+        assert to_numpy(getattr(a, f)).tobytes() == to_numpy(getattr(b, f)).tobytes(), f
 
 
 SMALL = [
@@ -267,6 +325,12 @@ SMALL = [
     ("noisy_top4", dict(T=5000, E=512, k=8, d_model=64, d_ff=64)),
     # 256-row tiles with a capacity between 160 and 256 (row tiles past the segment skipped)
     ("gshard_top2", dict(T=4000, E=16, capacity=200, d_model=296, d_ff=520)),
+    # first-choice priority drop order (GShard): binding capacities, k = 2, 3, 4, 8
+    ("gshard_top2", dict(T=2048, capacity=17, first_choice=True)),
+    ("gshard_top2", dict(T=1500, E=12, k=3, capacity=300, d_model=128, d_ff=256, first_choice=True)),
+    ("noisy_top4", dict(T=515, capacity=9, first_choice=True)),
+    ("noisy_top4", dict(T=64, E=8, k=8, capacity=50, first_choice=True)),
+    ("tiny_fp32", dict(T=200, capacity=60, first_choice=True)),
 ]
 
 
@@ -355,7 +419,7 @@ def test_twin_gate_columns(moelib, dev, name, over):
     _check_forward(c, fb, np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 48)])))
 
 
-def test_forward_is_deterministic(moelib, dev):
+def test_forward_small_is_deterministic(moelib, dev):
     from sparsely_gated_mixture_gate_amd.buffers import to_numpy
 
     c = _case("noisy_top4", T=4000)

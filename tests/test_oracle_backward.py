@@ -119,3 +119,23 @@ def test_dropped_assignments_get_no_expert_gradient(orc):
     b = orc.backward(spec, inp, dy)
     assert np.all(b["dw1"] == 0) and np.all(b["dw2"] == 0) and np.all(b["dx"] == 0)
     assert np.all(b["dw_gate"] == 0)
+
+
+def test_subset_backward_equals_full_rows(orc):
+    """The token / expert restriction used at full sizes returns exactly the
+    full backward's rows (same per-token arithmetic, batch statistics shared)."""
+    cfg = scaled(CONFIGS["noisy_top4"], T=60, E=8, k=2, d_model=16, d_ff=32)
+    inp = make_inputs(cfg)
+    spec = orc.LayerSpec.of(cfg, capacity=12)
+    dy = np.random.default_rng(4).standard_normal((cfg.T, cfg.d_model))
+    w = (0.2, 0.3, 0.4)
+    full = orc.backward(spec, inp, dy, w)
+    toks = np.array([0, 5, 17, 59])
+    exps = np.array([1, 6])
+    sub = orc.backward(spec, inp, dy, w, tokens=toks, experts=exps)
+    assert np.allclose(sub["dx"], full["dx"][toks], rtol=1e-12, atol=1e-14)
+    assert np.allclose(sub["dclean"], full["dclean"][toks], rtol=1e-12, atol=1e-14)
+    assert np.allclose(sub["du"], full["du"][toks], rtol=1e-12, atol=1e-14)
+    for e in exps:
+        assert np.allclose(sub["dw1"][e], full["dw1"][e], rtol=1e-12, atol=1e-14)
+        assert np.allclose(sub["dw2"][e], full["dw2"][e], rtol=1e-12, atol=1e-14)
