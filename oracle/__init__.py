@@ -57,6 +57,9 @@ def _lib():
             "oracle_expert_ffn_rows": ([i64, i32, i32, i32, i32, P, P, P, P, P, P], None),
             "oracle_combine": ([i64, P, i32, i32, P, P, P, P, P], None),
             "oracle_expert_bwd_rows": ([i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P], None),
+            "oracle_philox_words": ([ctypes.c_uint64, i64, i64, i32, P], None),
+            "oracle_normal_noise": ([ctypes.c_uint64, i64, i64, i32, P], None),
+            "oracle_normal_from_words_n": ([P, i64, P], None),
             "oracle_gate_bwd": ([i64, i64, i32, i32, i32, P, P, P, P, P, i32, P, P, P, dbl, P, P, P], None),
         }
         for name, (args, res) in sigs.items():
@@ -512,3 +515,29 @@ def backward(spec: LayerSpec, inp: dict, dy, loss_weights=(0.0, 0.0, 0.0), token
 def bf16_widen(a) -> np.ndarray:
     """bf16 bit patterns -> float64 (exact)."""
     return (np.ascontiguousarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# counter-based standard-normal noise (Shazeer et al. summary page, "Noisy
+# Top-K Gating": StandardNormal()); see moe_oracle.c for the definition
+# --------------------------------------------------------------------------
+def philox_words(seed: int, rows: int, cols: int, row0: int = 0) -> np.ndarray:
+    """Philox4x32-10 output words [rows, cols, 4] of counters (col, row lo, row hi, 0)."""
+    out = np.empty((rows, cols, 4), np.uint32)
+    _lib().oracle_philox_words(int(seed), int(row0), int(rows), int(cols), _p(out))
+    return out
+
+
+def normal_noise(seed: int, rows: int, cols: int, row0: int = 0) -> np.ndarray:
+    """Standard normals [rows, cols] fp32: Box-Muller on the first two Philox words."""
+    out = np.empty((rows, cols), np.float32)
+    _lib().oracle_normal_noise(int(seed), int(row0), int(rows), int(cols), _p(out))
+    return out
+
+
+def normal_from_words(words) -> np.ndarray:
+    """The transform alone: words [..., 2] uint32 -> standard normals fp32."""
+    w = np.ascontiguousarray(words, np.uint32).reshape(-1, 2)
+    out = np.empty(w.shape[0], np.float32)
+    _lib().oracle_normal_from_words_n(_p(w), w.shape[0], _p(out))
+    return out

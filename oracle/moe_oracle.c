@@ -636,3 +636,131 @@ void oracle_gate_bwd(int64_t T, int64_t T_batch, int E, int k, int renormalize, 
     free(dsig);
   }
 }
+
+/* ======================================================================== */
+/* Standard-normal noise of the noisy gate ([Shazeer] "Noisy Top-K Gating":  */
+/* StandardNormal()), as a counter-based stream that any IEEE machine         */
+/* reproduces bit for bit. Element (row, col) under key `seed`:               */
+/*   words = Philox4x32-10(counter = (col, row low 32 bits, row high 32 bits, */
+/*           0), key = (seed low, seed high)) -- the counter-based generator  */
+/*           of Salmon, Moraes, Dror and Shaw ("Parallel Random Numbers: As   */
+/*           Easy as 1, 2, 3", SC 2011): ten rounds of two 32x32->64-bit      */
+/*           multiplies (0xD2511F53, 0xCD9E8D57) and xors with the key, the   */
+/*           key bumped by (0x9E3779B9, 0xBB67AE85) between rounds;          */
+/*   u1 = ((w0 >> 8) + 1) 2^-24 in (0, 1], u2 = (w1 >> 8) 2^-24 in [0, 1);   */
+/*   z  = sqrt(-2 ln u1) cos(2 pi u2)   (Box-Muller),                         */
+/* with ln and cos defined from correctly rounded fp32 +, -, *, /, fma and    */
+/* sqrt only: ln u1 = log1p(u1 - 1) for u1 >= 1/2, else e ln2 + log1p(m - 1)  */
+/* for u1 = m 2^e, m in [1, 2) (the canonical log1p above, whose series also  */
+/* holds on [-1/2, 0]; ln2 split into the same head and tail), and            */
+/* cos(2 pi u2) folded by symmetry to cos or sin of an angle in [0, pi/4]     */
+/* evaluated by Taylor polynomials (degree 10 and 11) in Horner form.         */
+/* ======================================================================== */
+static void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    c[1] = (uint32_t)p1;
+    c[3] = (uint32_t)p0;
+    c[0] = n0;
+    c[2] = n2;
+  }
+}
+
+static float ln_unit(float u) { /* u in [2^-24, 1] */
+  /* u >= 1/2: ln u = log1p(u - 1), u - 1 in [-1/2, 0] exact (the series of the  */
+  /* canonical log1p converges as fast there); the split below would cancel   */
+  if (u >= 0.5f) return oracle_log1p_unit(u - 1.0f);
+  uint32_t b;
+  memcpy(&b, &u, sizeof b);
+  const int e = (int)(b >> 23) - 127;
+  const uint32_t mb = (b & 0x7FFFFFu) | (127u << 23);
+  float m;
+  memcpy(&m, &mb, sizeof m);
+  const float lg = oracle_log1p_unit(m - 1.0f);
+  const float hi = ln2_head();
+  const float lo = (float)(0.69314718055994530942 - (double)hi);
+  const float fe = (float)e;
+  const float t = fmaf(fe, lo, lg);
+  return fe * hi + t;
+}
+
+static float cos_two_pi(float u) { /* u in [0, 1) */
+  float w = u >= 0.5f ? u - 1.0f : u; /* [-0.5, 0.5), exact */
+  float a = fabsf(w);
+  float sign = 1.0f;
+  if (a > 0.25f) {
+    a = 0.5f - a;
+    sign = -1.0f;
+  }
+  const float two_pi = (float)6.28318530717958647692;
+  float p;
+  if (a > 0.125f) { /* cos(2 pi a) = sin(2 pi (1/4 - a)) */
+    const float y = two_pi * (0.25f - a);
+    const float y2 = y * y;
+    float q = (float)(1.0 / 39916800.0);
+    q = fmaf(q, -y2, (float)(1.0 / 362880.0));
+    q = fmaf(q, -y2, (float)(1.0 / 5040.0));
+    q = fmaf(q, -y2, (float)(1.0 / 120.0));
+    q = fmaf(q, -y2, (float)(1.0 / 6.0));
+    q = fmaf(q, -y2, 1.0f);
+    p = y * q;
+  } else {
+    const float y = two_pi * a;
+    const float y2 = y * y;
+    float q = (float)(1.0 / 3628800.0);
+    q = fmaf(q, -y2, (float)(1.0 / 40320.0));
+    q = fmaf(q, -y2, (float)(1.0 / 720.0));
+    q = fmaf(q, -y2, (float)(1.0 / 24.0));
+    q = fmaf(q, -y2, 0.5f);
+    p = fmaf(q, -y2, 1.0f);
+  }
+  return sign * p;
+}
+
+float oracle_normal_from_words(uint32_t w0, uint32_t w1) {
+  const float u1 = (float)((w0 >> 8) + 1u) * 0x1p-24f;
+  const float u2 = (float)(w1 >> 8) * 0x1p-24f;
+  const float r = sqrtf(-2.0f * ln_unit(u1));
+  return r * cos_two_pi(u2);
+}
+
+void oracle_philox_words(uint64_t seed, int64_t row0, int64_t rows, int cols, uint32_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int c = 0; c < cols; ++c) {
+      const uint64_t row = (uint64_t)(row0 + r);
+      uint32_t ctr[4] = {(uint32_t)c, (uint32_t)row, (uint32_t)(row >> 32), 0u};
+      philox4x32_10(ctr, (uint32_t)seed, (uint32_t)(seed >> 32));
+      memcpy(out + 4 * (r * cols + c), ctr, sizeof ctr);
+    }
+}
+
+void oracle_normal_noise(uint64_t seed, int64_t row0, int64_t rows, int cols, float* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int c = 0; c < cols; ++c) {
+      const uint64_t row = (uint64_t)(row0 + r);
+      uint32_t ctr[4] = {(uint32_t)c, (uint32_t)row, (uint32_t)(row >> 32), 0u};
+      philox4x32_10(ctr, (uint32_t)seed, (uint32_t)(seed >> 32));
+      out[r * cols + c] = oracle_normal_from_words(ctr[0], ctr[1]);
+    }
+}
+
+void oracle_normal_from_words_n(const uint32_t* words, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_normal_from_words(words[2 * i], words[2 * i + 1]);
+}
+
+/* the two fp32 pieces of the transform, element-wise (tests) */
+void oracle_ln_unit_n(const float* u, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = ln_unit(u[i]);
+}
+void oracle_cos_two_pi_n(const float* u, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = cos_two_pi(u[i]);
+}
