@@ -160,13 +160,17 @@ def cpu_baseline(cfg, inp, budget_s):
 # --------------------------------------------------------------------------
 # rocprofv3 summaries
 # --------------------------------------------------------------------------
+GEMM_SOURCES = ("expert_gemm.hip", "lds_dma.h", "common.h")
+
+
 def source_hash() -> str:
-    """Hash of the HIP sources: counter data taken on other sources is stale."""
+    """Hash of the expert GEMM's sources: counter data taken on another version of
+    the kernel is stale."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparsely_gated_mixture_gate_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in GEMM_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

@@ -64,7 +64,7 @@ enum {
   MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2, MOE_OP_FORWARD = 3, MOE_OP_BACKWARD = 4,
   MOE_OP_ROUTE_HIER = 5, MOE_OP_FORWARD_HIER = 6
 };
-enum { MOE_GATE_AUTO = 0, MOE_GATE_CANONICAL = 1, MOE_GATE_FALLBACK = 2 };
+enum { MOE_GATE_AUTO = 0, MOE_GATE_CANONICAL = 1, MOE_GATE_FALLBACK = 2, MOE_GATE_EXPORT = 3 };
 enum { MOE_DROP_TOKEN_ORDER = 0, MOE_DROP_FIRST_CHOICE = 1 };
 
 typedef struct moe_params {
@@ -84,7 +84,12 @@ typedef struct moe_params {
                                 with logits_out use the canonical fp32 chains;
                               MOE_GATE_CANONICAL (1): canonical fp32 chains for every token;
                               MOE_GATE_FALLBACK (2): the MFMA path with every token sent through its
-                                canonical fallback (testing). Routing is identical in all modes. */
+                                canonical fallback (testing);
+                              MOE_GATE_EXPORT (3, moe_route only; bf16, E <= 256): MOE_GATE_AUTO,
+                                and logits_out [2][T][E] receives the certificate's inputs: the MFMA
+                                logits H (before any recompute) and, per entry, the bound on their
+                                distance to the canonical logits (auditing). Routing is identical in
+                                all modes. */
   double capacity_factor;  /* > 0: per-expert capacity C = ceil(capacity_factor * k * T / E); <= 0: none */
   int64_t capacity;        /* >= 0: explicit per-expert capacity C (overrides capacity_factor); < 0: unused */
   int32_t drop_order;      /* which assignments a full expert drops (MOE_DROP_*):
@@ -339,6 +344,25 @@ moe_status moe_backward(const moe_params* p, const void* x, const void* w_gate, 
  * Returns MOE_ERR_INVALID_ARG unless 0 <= n <= 6.
  */
 moe_status moe_set_phase_events(void* const* events, int n);
+
+/*
+ * moe_standard_normal -- the StandardNormal() noise of the noisy gate (Shazeer
+ * "Methode", Noisy Top-K Gating) drawn on the device as a counter-based stream,
+ * bit-identical on any machine that follows the definition:
+ *   out[r][c] = N(seed, row0 + r, c), r < rows, c < cols (row-major, fp32), where
+ *   N(seed, row, col): Philox4x32-10 (Salmon et al., SC 2011) of the counter
+ *   (col, row & 0xFFFFFFFF, row >> 32, 0) under the key (seed & 0xFFFFFFFF,
+ *   seed >> 32) gives words w0, w1; u1 = ((w0 >> 8) + 1) 2^-24, u2 = (w1 >> 8)
+ *   2^-24; N = sqrt(-2 ln u1) cos(2 pi u2), with ln, cos and sqrt evaluated from
+ *   correctly rounded fp32 operations (ln u = log1p(u - 1) for u >= 1/2, else
+ *   e ln2 + log1p(m - 1), log1p as in moe_route's softplus; cos folded to
+ *   [0, pi/4] and Taylor polynomials of degree 10 / 11).
+ * Use it to fill moe_route's `noise` [T,E] (row = token, col = expert): any
+ * slice of tokens can be drawn alone with its row0.
+ * out: device, rows * cols fp32. Errors: MOE_ERR_INVALID_ARG for negative
+ * sizes or a row range past 2^63.
+ */
+moe_status moe_standard_normal(uint64_t seed, int64_t row0, int64_t rows, int32_t cols, float* out, void* stream);
 
 /*
  * moe_canonical_softplus -- the softplus of the noisy gate (Shazeer "Methode",

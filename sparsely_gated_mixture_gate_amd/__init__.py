@@ -24,13 +24,14 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
 (MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_FORWARD, MOE_OP_BACKWARD, MOE_OP_ROUTE_HIER,
  MOE_OP_FORWARD_HIER) = range(7)
-MOE_GATE_AUTO, MOE_GATE_CANONICAL, MOE_GATE_FALLBACK = range(3)
+MOE_GATE_AUTO, MOE_GATE_CANONICAL, MOE_GATE_FALLBACK, MOE_GATE_EXPORT = range(4)
 MOE_DROP_TOKEN_ORDER, MOE_DROP_FIRST_CHOICE = range(2)
 
 EXPORTED = (
     "moe_status_string", "moe_last_error", "moe_capacity", "moe_max_rows", "moe_workspace_size",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_canonical_softplus",
     "moe_set_phase_events", "moe_dispatch_noalloc", "moe_backward", "moe_route_hier", "moe_forward_hier",
+    "moe_standard_normal",
 )
 
 
@@ -88,6 +89,7 @@ def _load():
         "moe_canonical_softplus": ([P, P, i64, P], i32),
         "moe_set_phase_events": ([ctypes.POINTER(P), i32], i32),
         "moe_dispatch_noalloc": ([PP, P, P, P, P, P, P, P, P], i32),
+        "moe_standard_normal": ([ctypes.c_uint64, i64, i64, i32, P, P], i32),
         "moe_route_hier": ([PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
         "moe_forward_hier": ([PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
         "moe_backward": ([PP, P, P, P, P, P, P, P, P, ctypes.c_double, ctypes.c_double, ctypes.c_double,
@@ -236,6 +238,11 @@ def moe_backward(p, x, w_gate, gate_bias, w_noise, noise, w1, w2, dy, loss_weigh
                               _ptr(w1), _ptr(w2), _ptr(dy), ws_, wi, wl, _ptr(dx), _ptr(dw_gate), _ptr(dgate_bias),
                               _ptr(dw_noise), _ptr(dw1), _ptr(dw2), _ptr(dlogits), wp, wn, _stream(stream)),
            "moe_backward")
+
+
+def moe_standard_normal(seed, rows, cols, out, row0=0, stream=None):
+    _check(lib().moe_standard_normal(int(seed), int(row0), int(rows), int(cols), _ptr(out), _stream(stream)),
+           "moe_standard_normal")
 
 
 def moe_canonical_softplus(z, out, stream=None):

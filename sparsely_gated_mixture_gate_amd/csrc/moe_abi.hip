@@ -20,6 +20,7 @@ constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
 static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
 
 hipError_t launch_softplus(const float* z, float* out, int64_t n, hipStream_t s);
+hipError_t launch_normal_noise(uint64_t seed, int64_t row0, int64_t rows, int cols, float* out, hipStream_t s);
 
 namespace {
 
@@ -65,8 +66,8 @@ moe_status check_params(const moe_params* p) {
   if (p->act != MOE_ACT_RELU && p->act != MOE_ACT_GELU) return fail(MOE_ERR_INVALID_ARG, "act = %d", p->act);
   if (p->renormalize != 0 && p->renormalize != 1)
     return fail(MOE_ERR_INVALID_ARG, "renormalize = %d (0 or 1)", p->renormalize);
-  if (p->gate_mode < MOE_GATE_AUTO || p->gate_mode > MOE_GATE_FALLBACK)
-    return fail(MOE_ERR_INVALID_ARG, "gate_mode = %d (0, 1 or 2)", p->gate_mode);
+  if (p->gate_mode < MOE_GATE_AUTO || p->gate_mode > MOE_GATE_EXPORT)
+    return fail(MOE_ERR_INVALID_ARG, "gate_mode = %d (0, 1, 2 or 3)", p->gate_mode);
   if (p->T * (int64_t)p->k >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*k = %lld >= 2^31", (long long)(p->T * p->k));
   if (isnan(p->capacity_factor)) return fail(MOE_ERR_INVALID_ARG, "capacity_factor is NaN");
@@ -617,6 +618,11 @@ moe_status moe_route(const moe_params* p, const void* x, const void* w_gate, con
   }
   REQUIRE_PTR(counts_routed, "counts_routed");
   if (aux_out && !aligned16(aux_out)) return fail(MOE_ERR_INVALID_ARG, "aux_out is not 16-byte aligned");
+  if (p->gate_mode == MOE_GATE_EXPORT) {
+    if (!logits_out) return fail(MOE_ERR_INVALID_ARG, "MOE_GATE_EXPORT writes into logits_out, which is NULL");
+    if (p->dtype != MOE_BF16 || p->E > 256)
+      return fail(MOE_ERR_UNSUPPORTED, "MOE_GATE_EXPORT needs the certified MFMA gate (bf16, E <= 256)");
+  }
   if ((st = check_ws(p, MOE_OP_ROUTE, w_noise != nullptr, ws, ws_bytes)) != MOE_OK) return st;
   Carver c(ws);
   const RouteWs w = carve_route(c, p, w_noise != nullptr);
@@ -933,6 +939,15 @@ moe_status moe_set_phase_events(void* const* events, int n) {
   if (n < 0 || n > kPhaseEvents) return fail(MOE_ERR_INVALID_ARG, "n = %d outside [0, %d]", n, kPhaseEvents);
   for (int i = 0; i < kPhaseEvents; ++i) g_phase_ev[i] = (events && i < n) ? events[i] : nullptr;
   return MOE_OK;
+}
+
+// Counter-based standard-normal noise (see include/moe.h).
+moe_status moe_standard_normal(uint64_t seed, int64_t row0, int64_t rows, int32_t cols, float* out, void* stream) {
+  if (rows < 0 || cols < 0 || row0 < 0) return fail(MOE_ERR_INVALID_ARG, "rows, cols and row0 must be >= 0");
+  if (rows * (int64_t)cols > 0 && !out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  if (rows > 0 && (uint64_t)(row0 + rows - 1) < (uint64_t)row0) return fail(MOE_ERR_INVALID_ARG, "row range overflows");
+  const hipError_t e = launch_normal_noise(seed, row0, rows, cols, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "noise launch");
 }
 
 // Canonical softplus of the noisy gate, element-wise (z, out: n fp32 device values).

@@ -613,7 +613,8 @@ hipError_t launch_logits(const RouteLaunch& a, bool noisy, hipStream_t s) {
 
 int route_partial_blocks(int64_t T, int E, int dtype, int gate_mode, bool logits_out) {
   if (T <= 0) return 0;
-  const bool fused = route_fused_supported(dtype, E) && gate_mode != 1 && !logits_out;
+  // gate mode 3 exports the certified gate's logits and bounds through logits_out
+  const bool fused = route_fused_supported(dtype, E) && gate_mode != 1 && (!logits_out || gate_mode == 3);
   const int tpb = fused ? route_fused_tokens(T) : 64;
   return (int)((T + tpb - 1) / tpb);
 }
@@ -627,7 +628,8 @@ hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
   const bool noisy = a.w_noise != nullptr;
   const int nblk = route_partial_blocks(a.T, a.E, a.dtype, a.gate_mode, a.logits_out != nullptr);
   hipError_t err = hipSuccess;
-  const bool fused = route_fused_supported(a.dtype, a.E) && a.gate_mode != 1 && a.logits_out == nullptr;
+  const bool fused =
+      route_fused_supported(a.dtype, a.E) && a.gate_mode != 1 && (a.logits_out == nullptr || a.gate_mode == 3);
   if (a.T > 0 && fused) {
     const LogitBufs lb = logit_bufs(a, noisy);
     err = launch_route_fused(a, noisy, a.gate_mode == 2 ? 1 : 0, lb.CL, lb.SG, route_lpad(a.E), s);

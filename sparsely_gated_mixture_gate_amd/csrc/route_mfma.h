@@ -67,6 +67,7 @@ struct FusedArgs {
   float* part_imp;
   float* part_load;
   int32_t* part_cnt;
+  float* dbg;  // or null: [2][T][E] the MFMA logits and their bounds (MOE_GATE_EXPORT)
 };
 
 namespace {
@@ -360,6 +361,10 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
         spv[j] = sp;
         hv[j] = e < E ? h : -INFINITY;
         if (e < E) bmax = fmaxf(bmax, bh);
+        if (a.dbg && e < E && m < rows) {  // the certificate's inputs, for auditing
+          a.dbg[t * E + e] = h;
+          a.dbg[(a.T + t) * E + e] = bh;
+        }
         if (e < EP) Hs[m * HS + e] = hv[j];
       }
       if constexpr (NOISY) {

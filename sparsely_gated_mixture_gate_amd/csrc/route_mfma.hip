@@ -101,6 +101,7 @@ hipError_t launch_route_fused(const RouteLaunch& a, bool noisy, int force_fallba
   fa.part_imp = a.part_imp;
   fa.part_load = a.part_load;
   fa.part_cnt = a.part_cnt;
+  fa.dbg = a.gate_mode == 3 ? a.logits_out : nullptr;
   const int kk = a.k + 1 < a.E ? a.k + 1 : a.E;
   if (EP == 64) return noisy ? launch_fused_kk<64, true>(kk, fa, s) : launch_fused_kk<64, false>(kk, fa, s);
   if (EP == 128) return noisy ? launch_fused_kk<128, true>(kk, fa, s) : launch_fused_kk<128, false>(kk, fa, s);
