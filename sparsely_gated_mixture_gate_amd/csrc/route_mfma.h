@@ -331,6 +331,14 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
       }
     }
   }
+  // the gate bias of this lane's experts (the same for all its token rows), loaded once
+  float biasv[NE][4];
+#pragma unroll
+  for (int ni = 0; ni < NE; ++ni) {
+    const int e0 = NOISY ? 32 * wn + 16 * ni + 4 * g : wn * (16 * NI) + ni * 16 + 4 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) biasv[ni][j] = (a.bias && e0 + j < E) ? a.bias[e0 + j] : 0.0f;
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
     const int m = wm * (16 * MI) + mi * 16 + s;  // token row of this lane
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
       for (int j = 0; j < 4; ++j) {
         const int e = e0 + j;
         float cl = acc[mi][ni][j];
-        if (a.bias && e < E) cl = cl + a.bias[e];
+        if (a.bias && e < E) cl = cl + biasv[ni][j];
         const float bcl = KB * qs[mi][ni][j] * (1.0f + 0x1.0p-22f) + 0x1.0p-22f * fabsf(cl);
         float h = cl, bh = bcl, sp = 0.0f;
         if constexpr (NOISY) {
@@ -674,8 +682,9 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     // x rows and weight columns gathered into LDS as fp32 by all threads, and each
     // chain run by one thread from LDS (one fma per step), in rounds of as many
     // pairs as the LDS holds. The
-    // forced fallback, and blocks with more pairs than threads (or than 16 rounds),
-    // recompute whole rows instead (below).
+    // forced fallback, and blocks with more pairs than threads or whose pairs need more
+    // staging rounds than whole rows do (16 tokens a round), recompute whole rows
+    // instead (below).
     int* pair_tok = reinterpret_cast<int*>(smem + OFF_CV);  // [512] token row of each pair
     int* pair_e = pair_tok + 512;                            // [512] its expert
     constexpr int OFF_ST = OFF_CV + 4096;                    // staged operands, one block per pair
@@ -728,7 +737,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
         if (lane < nflag) resi[flist_s[lane] * RS + 22] = v - c;
         if (lane == 63) {
           np_s = v;
-          fb_full_s = (v > 512 || v > 16 * maxp) ? 1 : 0;
+          // whole rows when the pairs need more staging rounds than rows of 16 tokens would
+          fb_full_s = (v > 512 || (v + maxp - 1) / maxp > (nflag_s + 15) / 16) ? 1 : 0;
         }
       }
       __syncthreads();
