@@ -682,9 +682,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     // x rows and weight columns gathered into LDS as fp32 by all threads, and each
     // chain run by one thread from LDS (one fma per step), in rounds of as many
     // pairs as the LDS holds. The
-    // forced fallback, and blocks with more pairs than threads or whose pairs need more
-    // staging rounds than whole rows do (16 tokens a round), recompute whole rows
-    // instead (below).
+    // forced fallback, and blocks with more pairs than threads (or than 16 rounds),
+    // recompute whole rows instead (below).
     int* pair_tok = reinterpret_cast<int*>(smem + OFF_CV);  // [512] token row of each pair
     int* pair_e = pair_tok + 512;                            // [512] its expert
     constexpr int OFF_ST = OFF_CV + 4096;                    // staged operands, one block per pair
@@ -737,8 +736,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
         if (lane < nflag) resi[flist_s[lane] * RS + 22] = v - c;
         if (lane == 63) {
           np_s = v;
-          // whole rows when the pairs need more staging rounds than rows of 16 tokens would
-          fb_full_s = (v > 512 || (v + maxp - 1) / maxp > (nflag_s + 15) / 16) ? 1 : 0;
+          fb_full_s = (v > 512 || v > 16 * maxp) ? 1 : 0;
         }
       }
       __syncthreads();
