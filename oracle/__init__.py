@@ -36,9 +36,14 @@ RELU, GELU = 0, 1
 def _lib():
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        lib = ctypes.CDLL(_build.LIB)
+        # MOE_ORACLE_LIB: another build of moe_oracle.c (the sanitizer test loads an
+        # ASan/UBSan build through it)
+        path = os.environ.get("MOE_ORACLE_LIB")
+        if path is None:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
         sigs = {

@@ -17,7 +17,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# MOE_LIB names another build of the same library (the host-sanitizer test loads an
+# AddressSanitizer build through it); by default the in-tree libmoe.so
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
