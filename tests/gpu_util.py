@@ -84,3 +84,47 @@ def sample_rows(offsets: np.ndarray, n_random: int, seed: int = 0) -> np.ndarray
     rng = np.random.default_rng(seed)
     rows = np.concatenate([np.array(edges, np.int64), rng.integers(0, R, n_random)])
     return np.unique(rows)
+
+
+GUARD = 4096
+PAT = 0xA5
+
+
+class Arena:
+    """Output buffers as views between guard bands of the byte PAT (GUARD bytes on each
+    side, the view 256-byte aligned); check() asserts that no guard byte changed."""
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.bufs = []
+
+    def alloc(self, shape, dtype, fill=float("nan")):
+        import torch
+
+        shape = tuple(int(s) for s in shape)
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        raw = torch.full((n + 2 * GUARD + 256,), PAT, dtype=torch.uint8, device=self.dev)
+        off = GUARD + (-(raw.data_ptr() + GUARD)) % 256  # 256-byte aligned view
+        view = raw[off:off + n].view(dtype).view(shape)
+        if fill is not None and n:
+            view.fill_(fill if dtype.is_floating_point else -1)
+        self.bufs.append((raw, off, n))
+        return view
+
+    def workspace(self, nbytes):
+        import torch
+
+        return self.alloc((max(int(nbytes), 1),), torch.uint8, fill=None)
+
+    def check(self, what):
+        import torch
+
+        if any(raw.is_cuda for raw, _, _ in self.bufs):
+            torch.cuda.synchronize()
+        for i, (raw, off, n) in enumerate(self.bufs):
+            h = raw.cpu().numpy()
+            lo = np.flatnonzero(h[:off] != PAT)
+            hi = np.flatnonzero(h[off + n:] != PAT)
+            assert lo.size == 0 and hi.size == 0, (
+                f"{what}: buffer {i} ({n} bytes): guard bytes changed, {lo.size} before it "
+                f"(first at -{off - lo[-1] if lo.size else 0}), {hi.size} after it (first at +{hi[0] if hi.size else 0})")
