@@ -243,6 +243,9 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   };
 
   const int wm = wave / WN_W, wn = wave % WN_W;
+  // 16-token MFMA row tiles of this wave that hold tokens of the block (the tile has
+  // 64 rows; 32-token blocks and the last block leave the rest idle)
+  const int mact = __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - wm * 16 * MI + 15) / 16)));
   const int g = lane >> 4, s = lane & 15;
   // acc: the logits; qs: Q + S, i.e. |acc| after every k-step (the step before
   // this one; the last is added after the loop) plus the sign-cleared MFMA
@@ -251,22 +254,29 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = qs[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  auto add_q = [&]() {
+  // PART: only the first mact row tiles hold tokens (a compile-time switch, so full
+  // tiles keep a branch-free loop)
+  auto add_q = [&](auto part_c) {
+    constexpr bool PART = decltype(part_c)::value;
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      if (PART && i >= mact) break;
 #pragma unroll
       for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) qs[i][j][r] += fabsf(acc[i][j][r]);
+    }
   };
 
-  auto compute = [&](int st) {
-    add_q();
+  auto compute = [&](int st, auto part_c) {
+    constexpr bool PART = decltype(part_c)::value;
+    add_q(part_c);
     const uint4* sA = &smem_u4[st * CH];
     lds_char* sB = (lds_char*)(&smem_u4[st * CH + A_CH]);
     uint4 af[MI], bfr[NI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
+      if (PART && mi >= mact) break;
       const int row = wm * (16 * MI) + mi * 16 + s;
       af[mi] = sA[row * 4 + (g ^ swz4(row))];
     }
@@ -285,7 +295,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     }
     const uint4 m7 = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
+      if (PART && mi >= mact) break;
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[ni]),
@@ -293,19 +304,24 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
         qs[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[ni] & m7),
                                                              __builtin_bit_cast(bf16x8, af[mi] & m7), qs[mi][ni], 0, 0, 0);
       }
+    }
   };
 
   const int nk = (d + kBK - 1) / kBK;
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t)
     if (t < nk) issue(t);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_stages<kStages - 2>(ld, min(kStages - 2, nk - 1 - kt));
-    block_barrier();
-    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
-    compute(kt % kStages);
-  }
-  add_q();
+  auto main_loop = [&](auto part_c) {
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_stages<kStages - 2>(ld, min(kStages - 2, nk - 1 - kt));
+      block_barrier();
+      if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+      compute(kt % kStages, part_c);
+    }
+    add_q(part_c);
+  };
+  if (mact == MI) main_loop(std::false_type{});
+  else main_loop(std::true_type{});
   __syncthreads();  // the ring is dead from here on; its LDS holds the logit tile and the selection state
 
   // ---- epilogue: clean logit (+ bias), softplus, H and the bound ------------------
@@ -317,6 +333,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   if constexpr (NOISY) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
+      if (mi >= mact) break;
       const int64_t t = t0 + min(wm * (16 * MI) + mi * 16 + s, rows - 1);
 #pragma unroll
       for (int ni = 0; ni < NE; ++ni) {
@@ -343,6 +360,16 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   for (int mi = 0; mi < MI; ++mi) {
     const int m = wm * (16 * MI) + mi * 16 + s;  // token row of this lane
     const int64_t t = t0 + m;
+    if (mi >= mact) {  // no token in this row tile: its logit rows are never selected
+#pragma unroll
+      for (int ni = 0; ni < NE; ++ni) {
+        const int e0 = NOISY ? 32 * wn + 16 * ni + 4 * g : wn * (16 * NI) + ni * 16 + 4 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (e0 + j < EP) Hs[m * HS + e0 + j] = -INFINITY;
+      }
+      continue;
+    }
     float bmax = 0.0f;
 #pragma unroll
     for (int ni = 0; ni < NE; ++ni) {
@@ -963,12 +990,12 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   // ---- phase 3, lane = expert: sums over token slices in token order ---------------
   constexpr int G = EP / 64;   // expert groups of 64
   constexpr int TS = 8 / G;    // token slices
-  constexpr int TL = kTok / TS;
   const int gq = wave % G, ts = wave / G;
   const int e = gq * 64 + lane;
   if (e < E) {
     const bool have_in = KK > k;
-    const int tl_lo = min(rows, ts * TL), tl_hi = min(rows, tl_lo + TL);
+    const int tls = (rows + TS - 1) / TS;  // tokens per slice
+    const int tl_lo = min(rows, ts * tls), tl_hi = min(rows, tl_lo + tls);
     float p_sum = 0.0f, imp_sum = 0.0f, ld_sum = 0.0f;
     int cnt = 0;
     constexpr int TB = 8;  // tokens whose global loads are in flight together
