@@ -124,6 +124,39 @@ __device__ __forceinline__ void wait_stages(int ld, int rem) {
 }
 
 
+// Exchanges inside aligned groups of 8 lanes (DPP: quad_perm lane^1, quad_perm lane^2,
+// half-row mirror lane -> 7 - lane): after the three steps every lane of the group
+// holds the combination of the group's 8 values.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& v, int& i) {
+  const float ov = __int_as_float(dpp_mov<CTRL>(__float_as_int(v)));
+  const int oi = dpp_mov<CTRL>(i);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+__device__ __forceinline__ void best8(float& v, int& i) {  // first in (value desc, index asc)
+  best_step<kDppXor1>(v, i);
+  best_step<kDppXor2>(v, i);
+  best_step<kDppHalfMirror>(v, i);
+}
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, __int_as_float(dpp_mov<kDppXor1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_mov<kDppXor2>(__float_as_int(v))));
+  return fmaxf(v, __int_as_float(dpp_mov<kDppHalfMirror>(__float_as_int(v))));
+}
+__device__ __forceinline__ float sum8(float v) {
+  v += __int_as_float(dpp_mov<kDppXor1>(__float_as_int(v)));
+  v += __int_as_float(dpp_mov<kDppXor2>(__float_as_int(v)));
+  return v + __int_as_float(dpp_mov<kDppHalfMirror>(__float_as_int(v)));
+}
+
 template <int EP, bool NOISY, int KK>
 __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   constexpr int NCOL = NOISY ? 2 * EP : EP;
@@ -181,6 +214,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   __shared__ uint4 smem_u4[SMEM / 16];
   __shared__ float bmax_s[kTok];
   __shared__ int flist_s[kTok];
+  __shared__ int flag_s[kTok];  // token row not certified
   __shared__ int nflag_s;
   __shared__ int fb_full_s;  // the candidate pairs do not fit: the block recomputes whole rows
   __shared__ int np_s;       // candidate pairs of the block
@@ -539,9 +573,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     wsum[wave * 64 + lane] = s_w;
   };
 
-  // phase 2 (wave 0), lane = token: merge the 8 sorted lists, softmax, gates;
-  // certify = check the gaps (first pass) or accept (canonical logits)
-  // token tl's results from its top-KK values / indices (value desc, index asc),
+  // token row tl's results from its top-KK values / indices (value desc, index asc),
   // softmax max m and sum S: gates, load-estimator thresholds, outputs
   auto finish = [&](int tl, const float (&sel_v)[KK], const int (&sel_i)[KK], float m, float S) {
     const int64_t t = t0 + tl;
@@ -589,53 +621,63 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     }
   };
 
-  // phase 2 (wave 0), lane = token: merge the 8 sorted lists and certify the
-  // token; certified tokens get their results, the others return false
-  auto merge = [&]() -> bool {
-    float sel_v[KK];
-    int sel_i[KK];
-    uint32_t heads = 0;  // 4 bits per list: index of its next candidate
+  // phase 2, all waves: 8 lanes per token row (wave w: rows 8w .. 8w+7, lane = 8 * row
+  // + list), lane j holding the sorted top-KK list of scan wave j. Each of the KK rounds
+  // takes the best list head of the group (value desc, index asc; expert ids are unique
+  // across the lists) and advances the list it came from; the softmax max and sum
+  // combine the same way. The group's first lane certifies the row (gaps against
+  // twice its largest bound) and writes its results, or flags it.
+  auto merge8 = [&]() {
+    const int j = lane & 7;
+    const int m = wave * 8 + (lane >> 3);
+    float lv[KK];
+    int li[KK];
 #pragma unroll
     for (int r = 0; r < KK; ++r) {
-      float best = -INFINITY;
-      int bi = 0x7FFFFFFF, bw = -1;
-      for (int w = 0; w < 8; ++w) {
-        const int hd = (int)((heads >> (4 * w)) & 15u);
-        if (hd >= KK) continue;
-        const float v = cand_v[(w * KK + hd) * 64 + lane];
-        const int i = cand_i[(w * KK + hd) * 64 + lane];
-        if (i == 0x7FFFFFFF) continue;
-        if (bw < 0 || better(v, i, best, bi)) {
-          best = v;
-          bi = i;
-          bw = w;
-        }
-      }
-      if (bw >= 0) heads += 1u << (4 * bw);
-      sel_v[r] = best;
-      sel_i[r] = bi;
+      lv[r] = cand_v[(j * KK + r) * 64 + m];
+      li[r] = cand_i[(j * KK + r) * 64 + m];
     }
-    if (lane >= rows) return true;  // rows past the block's tokens: nothing to route
+    float sel_v[KK];
+    int sel_i[KK];
+    int h = 0;  // this list's next entry
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
+      float v = -INFINITY;
+      int i = 0x7FFFFFFF;
+#pragma unroll
+      for (int q = 0; q < KK; ++q)
+        if (q == h) {
+          v = lv[q];
+          i = li[q];
+        }
+      float bv = v;
+      int bi = i;
+      best8(bv, bi);
+      sel_v[r] = bv;
+      sel_i[r] = bi;
+      if (bi != 0x7FFFFFFF && i == bi) ++h;
+    }
+    const float mw = wmax[j * 64 + m];
+    const float mt = max8(mw);
+    const float S = sum8(mw != -INFINITY ? wsum[j * 64 + m] * fast_exp(mw - mt) : 0.0f);
+    if (j != 0) return;
+    if (m >= rows) {  // rows past the block's tokens: nothing to route
+      flag_s[m] = 0;
+      return;
+    }
     bool ok = !a.force_fallback;
-    const float b2 = 2.0f * bmax_s[lane];
+    const float b2 = 2.0f * bmax_s[m];
     const int ngap = min(k, KK - 1);
 #pragma unroll
     for (int r = 0; r + 1 < KK; ++r)
       if (r < ngap) ok = ok && (sel_v[r] - sel_v[r + 1] > b2);  // false for NaN
+    flag_s[m] = ok ? 0 : 1;
     if (!ok) {
       // candidates of the canonical top-KK: every expert with v >= v_KK - 2B (see the fallback)
-      res[lane * RS + 20] = sel_v[KK - 1] - b2;
-      return false;
+      res[m * RS + 20] = sel_v[KK - 1] - b2;
+      return;
     }
-    float m = -INFINITY;
-    for (int w = 0; w < 8; ++w) m = fmaxf(m, wmax[w * 64 + lane]);
-    float S = 0.0f;
-    for (int w = 0; w < 8; ++w) {
-      const float mw = wmax[w * 64 + lane];
-      if (mw != -INFINITY) S += wsum[w * 64 + lane] * fast_exp(mw - m);
-    }
-    finish(lane, sel_v, sel_i, m, S);
-    return true;
+    finish(m, sel_v, sel_i, mt, S);
   };
 
   // one wave, lane = expert (e = lane + 64 c): top-KK and softmax of token tl
@@ -686,10 +728,12 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   if (a.tpb <= 32) scan_halves();
   else scan();
   __syncthreads();
-  if (wave == 0) {
-    const bool ok = merge();
-    const uint64_t bad = __ballot(!ok);
-    if (!ok) flist_s[__builtin_amdgcn_mbcnt_hi((uint32_t)(bad >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bad, 0u))] = lane;
+  merge8();
+  __syncthreads();
+  if (wave == 0) {  // flagged rows in token order
+    const bool bad_l = flag_s[lane] != 0;
+    const uint64_t bad = __ballot(bad_l);
+    if (bad_l) flist_s[__builtin_amdgcn_mbcnt_hi((uint32_t)(bad >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bad, 0u))] = lane;
     if (lane == 0) nflag_s = __popcll(bad);
   }
   __syncthreads();
