@@ -151,10 +151,39 @@ __device__ __forceinline__ float max8(float v) {
   v = fmaxf(v, __int_as_float(dpp_mov<kDppXor2>(__float_as_int(v))));
   return fmaxf(v, __int_as_float(dpp_mov<kDppHalfMirror>(__float_as_int(v))));
 }
+// the same over a whole wave: the four 16-lane rows by DPP (row mirror lane -> 15 - lane
+// joins the two 8-lane halves), then the rows' results read from lanes 0, 16, 32, 48
+constexpr int kDppRowMirror = 0x140;
+__device__ __forceinline__ void best64(float& v, int& i) {
+  best8(v, i);
+  best_step<kDppRowMirror>(v, i);
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) {
+    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), r));
+    const int oi = __builtin_amdgcn_readlane(i, r);
+    if (better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  v = bv;
+  i = bi;
+}
 __device__ __forceinline__ float sum8(float v) {
   v += __int_as_float(dpp_mov<kDppXor1>(__float_as_int(v)));
   v += __int_as_float(dpp_mov<kDppXor2>(__float_as_int(v)));
   return v + __int_as_float(dpp_mov<kDppHalfMirror>(__float_as_int(v)));
+}
+__device__ __forceinline__ float sum64(float v) {
+  v = sum8(v);
+  v += __int_as_float(dpp_mov<kDppRowMirror>(__float_as_int(v)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 template <int EP, bool NOISY, int KK>
@@ -701,15 +730,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
           v = hv[c];
           i = lane + 64 * c;
         }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(v, off);
-        const int oi = __shfl_xor(i, off);
-        if (better(ov, oi, v, i)) {
-          v = ov;
-          i = oi;
-        }
-      }
+      best64(v, i);
       sel_v[r] = v;
       sel_i[r] = i;
       if (i != 0x7FFFFFFF && (i & 63) == lane) taken |= 1u << (i >> 6);
@@ -719,8 +740,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
 #pragma unroll
     for (int c = 0; c < G; ++c)
       if (lane + 64 * c < E) S += fast_exp(hv[c] - m);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+    S = sum64(S);
     if (lane == 0) finish(tl, sel_v, sel_i, m, S);
   };
 
