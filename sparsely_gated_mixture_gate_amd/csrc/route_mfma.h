@@ -176,6 +176,19 @@ __device__ __forceinline__ float sum8(float v) {
   v += __int_as_float(dpp_mov<kDppXor2>(__float_as_int(v)));
   return v + __int_as_float(dpp_mov<kDppHalfMirror>(__float_as_int(v)));
 }
+// value of lane ^ 32 / lane ^ 16 (v_permlane32_swap / v_permlane16_swap of two copies:
+// the first result holds the low half / even rows twice, the second the high half /
+// odd rows twice)
+__device__ __forceinline__ int xor32(int v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (threadIdx.x & 32) ? (int)r[0] : (int)r[1];
+}
+__device__ __forceinline__ float xor32(float v) { return __int_as_float(xor32(__float_as_int(v))); }
+__device__ __forceinline__ int xor16(int v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (threadIdx.x & 16) ? (int)r[0] : (int)r[1];
+}
+__device__ __forceinline__ float xor16(float v) { return __int_as_float(xor16(__float_as_int(v))); }
 __device__ __forceinline__ float sum64(float v) {
   v = sum8(v);
   v += __int_as_float(dpp_mov<kDppRowMirror>(__float_as_int(v)));
@@ -482,8 +495,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
       }
     }
     // lanes s, s+16, s+32, s+48 share the token row: max over them, then over waves
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    bmax = fmaxf(bmax, xor16(bmax));
+    bmax = fmaxf(bmax, xor32(bmax));
     if (g == 0) atomicMax(reinterpret_cast<int*>(&bmax_s[m]), __float_as_int(bmax));  // non-negative floats order as ints
   }
   __syncthreads();
@@ -578,14 +591,14 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     for (int c = 0; c < EH; ++c)
       if (e_lo + c < e_hi) s_h += fast_exp(hv[c] - m_h);
     const bool have_h = e_lo < e_hi;
-    const bool have_o = __shfl_xor((int)have_h, 32) != 0;
-    const float m_o = __shfl_xor(m_h, 32), s_o = __shfl_xor(s_h, 32);
+    const bool have_o = xor32((int)have_h) != 0;
+    const float m_o = xor32(m_h), s_o = xor32(s_h);
     float ov[KK];
     int oi[KK];
 #pragma unroll
     for (int r = 0; r < KK; ++r) {
-      ov[r] = __shfl_xor(bv[r], 32);
-      oi[r] = __shfl_xor(bi[r], 32);
+      ov[r] = xor32(bv[r]);
+      oi[r] = xor32(bi[r]);
     }
 #pragma unroll
     for (int r = 0; r < KK; ++r)
