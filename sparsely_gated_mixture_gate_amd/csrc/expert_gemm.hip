@@ -260,7 +260,8 @@ __global__ __launch_bounds__(64 * NW, (BM / (NW / (BN / WNT))) * WNT > 8192 ? 1 
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const uint32_t dst = lds0 + (uint32_t)((st * STAGE_CH + A_CH + i * NT + wave * 64) * 16);
-      // SKIP: one M-tile per expert, so each weight byte is read by this workgroup only
+      // SKIP shapes: most experts fit one M-tile, so their weight bytes are read by one
+      // workgroup row only and are streamed past the caches
       if constexpr (SKIP)
         load_to_lds_nt(__builtin_amdgcn_readfirstlane(dst), last ? voffB_last[i] : voffB[i], rsB, soffB);
       else
@@ -576,8 +577,10 @@ hipError_t launch_ffn_act(const FfnLaunch& a, hipStream_t s) {
     case kTiles256: return launch_bf16<256, 32, 4, ACT, false, true, 8, 128>(a, s);
     // about one M-tile of rows per expert, no capacity: 256-column tiles on both layers
     // (twice the tiles of 512-column ones, so the tile rounds of a skewed routing stay
-    // fuller: layer 2 of noisy_top4 has ~320 M-tiles for 256 CUs)
-    default: return launch_bf16<128, 32, 3, ACT, false, false, 8, 64, 256>(a, s);
+    // fuller: layer 2 of noisy_top4 has ~320 M-tiles for 256 CUs); most segments fill
+    // part of their one tile, so MFMA row tiles past the segment are skipped and the
+    // weight panels are streamed with the non-temporal hint
+    default: return launch_bf16<128, 32, 3, ACT, true, false, 8, 64, 256>(a, s);
   }
 }
 
