@@ -21,8 +21,10 @@
 //     (layer 1, 3 stages) and 160 x 384 x 32 (layer 2, 4 stages), capacity <= 256
 //     -> 256 x 256 x 32 (4 stages), both one M-tile per expert with 16-row MFMA
 //     tiles past the segment skipped and their A rows loaded as zero; otherwise
-//     about one tile of rows per expert -> 128 x 512 x 32 (3 stages), large
-//     segments -> 256 x 256 x 32 (4 stages). Where weights stream from HBM, wide
+//     about one tile of rows per expert -> 128 x 256 x 32 (3 stages, row tiles past
+//     the segment skipped), large segments -> 256 x 256 x 64 (layer 1, 2 stages,
+//     unswizzled activation rows: one 128-byte L2 request per row and k-tile) and
+//     256 x 256 x 32 (layer 2, 4 stages). Where weights stream from HBM, wide
 //     N-tiles re-read each expert's rows fewer times and read fewer LDS operand
 //     bytes per weight byte (those reads compete with the weight loads). Both operands go
 //     HBM -> LDS in their HBM layout by direct-to-LDS buffer loads (16-byte
@@ -134,10 +136,13 @@ __device__ __forceinline__ bool schedule_tile(const int32_t* __restrict__ tile_s
   return true;
 }
 
+// A rows of 64-wide k-tiles (8 chunks, 128 bytes) stay unswizzled: 8 lanes then load a
+// row's 128 bytes in address order, which the vector L1 fetches as one request (a swizzled
+// row costs two 64-byte requests, and the L1 keeps a bounded number in flight).
 template <int RC>
 __device__ __forceinline__ int swz_a_rc(int row) {
   if constexpr (RC == 8) {
-    return (row ^ (row >> 3)) & 7;
+    return 0;
   } else {
     return (row >> 2) & 3;
   }
@@ -574,7 +579,10 @@ hipError_t launch_ffn_act(const FfnLaunch& a, hipStream_t s) {
     // layer 2 384 columns (two tiles of a 768-wide output)
     case kTiles160Skip: return launch_bf16<160, 32, 4, ACT, true, false, 8, 96, 384, 32, 3, 512, 128>(a, s);
     case kTiles256Skip: return launch_bf16<256, 32, 4, ACT, true, true>(a, s);
-    case kTiles256: return launch_bf16<256, 32, 4, ACT, false, true, 8, 128>(a, s);
+    // layer 1 (K = d_model, the shorter) in 64-wide k-tiles, 2 stages: one 128-byte request per
+    // activation row and k-tile instead of two (2.39 -> 2.28 ms at dropless_top1); layer 2
+    // keeps 32-wide k-tiles in 4 stages (two 64 KB stages left its long K 27% slower)
+    case kTiles256: return launch_bf16<256, 32, 4, ACT, false, true, 8, 128, 256, 64, 2, 256, 128>(a, s);
     // about one M-tile of rows per expert, no capacity: 256-column tiles on both layers
     // (twice the tiles of 512-column ones, so the tile rounds of a skewed routing stay
     // fuller: layer 2 of noisy_top4 has ~320 M-tiles for 256 CUs); most segments fill

@@ -321,6 +321,12 @@ SMALL = [
     ("dropless_top1", dict(T=999, d_model=512, d_ff=640)),
     # 256-row expert tiles: ragged K and N, more tiles than CUs (several per persistent block)
     ("dropless_top1", dict(T=40000, E=4, d_model=200, d_ff=328)),
+    # 256-row tiles with d and f multiples of 64 (activation super-stages of 64 k): short K
+    # (one or two super-stages, fewer than the rings hold), partial tiles, gathered and
+    # scattered rows, top-2 through the combine
+    ("dropless_top1", dict(T=20000, E=6, d_model=192, d_ff=320)),
+    ("gshard_top2", dict(T=12000, E=8, d_model=64, d_ff=128)),
+    ("dropless_top1", dict(T=9000, E=2, d_model=128, d_ff=64)),
     # count table too large for in-block prefixes (separate scan kernel)
     ("noisy_top4", dict(T=5000, E=512, k=8, d_model=64, d_ff=64)),
     # 256-row tiles with a capacity between 160 and 256 (row tiles past the segment skipped)
