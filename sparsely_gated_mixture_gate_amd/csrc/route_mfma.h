@@ -36,8 +36,10 @@
 // rounding-level effect, far inside the bf16 output tolerance).
 //
 // One block = 64 tokens, 512 threads (8 waves):
-//   GEMM: x tile [64][32] and weight tile [32][NCOL] per stage in an LDS ring
-//   of up to 8 stages (direct-to-LDS buffer loads), v_mfma_f32_16x16x32_bf16 with
+//   GEMM: x tile [64][BK] and weight tile [BK][NCOL] per stage in an LDS ring
+//   (direct-to-LDS buffer loads): BK = 64 and up to 4 stages for NCOL <= 128
+//   (each token's 128 bytes of a stage are one unswizzled L2 request), else
+//   BK = 32 and up to 8 stages (x rows XOR-swizzled); v_mfma_f32_16x16x32_bf16 with
 //   swapped operands (lane = 4 consecutive columns of one token); noisy: each
 //   wave's 64 columns are 32 experts' gate columns and the same experts' noise
 //   columns, so one lane holds both halves of an expert's logit.
@@ -80,7 +82,6 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kTok = 64;     // rows of the logit tile (a block routes 64 tokens, or 32)
-constexpr int kBK = 32;      // k per LDS stage (one MFMA k-step)
 
 
 __device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }  // x tile: 4 chunks per row
@@ -207,8 +208,12 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   constexpr int WM_W = 8 / WN_W;           // waves along tokens
   constexpr int MI = 4 / WM_W;             // 16-token MFMA tiles per wave
   constexpr int BCR = NCOL / 8;            // 16-byte chunks per weight row
-  constexpr int A_CH = kTok * 4;           // x chunks per stage
-  constexpr int B_CH = kBK * BCR;          // weight chunks per stage
+  // k per LDS stage: 64 where the weight tile stays small (then the x rows of a stage are
+  // 128 bytes, loaded unswizzled so that each is one L2 request), else 32 (x rows swizzled)
+  constexpr int SBK = NCOL <= 128 ? 64 : 32;
+  constexpr int XR = SBK / 8;              // x chunks per row per stage
+  constexpr int A_CH = kTok * XR;          // x chunks per stage
+  constexpr int B_CH = SBK * BCR;          // weight chunks per stage
   constexpr int CH = A_CH + B_CH;
   constexpr int NR = (CH + 511) / 512;     // load rounds per stage
   constexpr int HS = EP + 1;               // LDS row stride of the logit tile (floats)
@@ -216,8 +221,9 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   constexpr int KS = KK < 8 ? KK : 8;      // selectable slots
   constexpr int RS = 24;                   // res floats per token: m, S, thr_out, thr_in, sel[8], gate[8], pad
   static_assert(CH % 64 == 0 && WN_W * WM_W == 8 && MI >= 1 && (!NOISY || NI == 4), "shape");
-  // GEMM ring depth: as many 32-k stages as fit beside the other LDS use (at most 8)
-  constexpr int kStages = (144 * 1024) / (CH * 16) < 8 ? (144 * 1024) / (CH * 16) : 8;
+  // GEMM ring depth: as many stages as fit beside the other LDS use (at most 8 of 32 k, 4 of 64 k)
+  constexpr int kMaxStages = SBK == 64 ? 4 : 8;
+  constexpr int kStages = (144 * 1024) / (CH * 16) < kMaxStages ? (144 * 1024) / (CH * 16) : kMaxStages;
   static_assert(kStages >= 3, "ring");
   constexpr int RING = kStages * CH * 16;
   // After the GEMM the ring's LDS holds: the logit tile H and the per-token
@@ -294,8 +300,9 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     isA[i] = (i * 512 + wave * 64) < A_CH;
     ld += act[i] ? 1 : 0;
     if (c < A_CH) {
-      const int row = c >> 2, p = c & 3;
-      voff[i] = min(row, rows - 1) * d * 2 + ((p ^ swz4(row)) << 4);  // rows past T: clamped, never stored
+      const int row = c / XR, p = c % XR;
+      const int pc = SBK == 64 ? p : p ^ swz4(row);
+      voff[i] = min(row, rows - 1) * d * 2 + (pc << 4);  // rows past T: clamped, never stored
     } else {
       const int b = c - A_CH;
       const int kr = b / BCR, p = b % BCR;
@@ -312,9 +319,9 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
       if (!act[i]) continue;
       const uint32_t dst = lds0 + (uint32_t)((st * CH + i * 512 + wave * 64) * 16);
       if (isA[i])
-        load_to_lds(__builtin_amdgcn_readfirstlane(dst), voff[i] + kt * kBK * 2, rsX, 0);
+        load_to_lds(__builtin_amdgcn_readfirstlane(dst), voff[i] + kt * SBK * 2, rsX, 0);
       else
-        load_to_lds(__builtin_amdgcn_readfirstlane(dst), voff[i] + kt * kBK * NCOL * 2, rsW, 0);
+        load_to_lds(__builtin_amdgcn_readfirstlane(dst), voff[i] + kt * SBK * NCOL * 2, rsW, 0);
     }
   };
 
@@ -346,44 +353,48 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
 
   auto compute = [&](int st, auto part_c) {
     constexpr bool PART = decltype(part_c)::value;
-    add_q(part_c);
     const uint4* sA = &smem_u4[st * CH];
     lds_char* sB = (lds_char*)(&smem_u4[st * CH + A_CH]);
-    uint4 af[MI], bfr[NI];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      if (PART && mi >= mact) break;
-      const int row = wm * (16 * MI) + mi * 16 + s;
-      af[mi] = sA[row * 4 + (g ^ swz4(row))];
-    }
+    for (int ks = 0; ks < SBK / 32; ++ks) {  // one 32-wide MFMA k-step each
+      add_q(part_c);
+      uint4 af[MI], bfr[NI];
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      // transposing read: lane L of a 16-lane group receives W[k0 .. k0+3][n + L]
-      const int krow = 8 * g + (s >> 2);
-      const int ncol = wn * (16 * NI) + ni * 16 + 4 * (s & 3);
-      const int c = ncol >> 3;
-      const int b0 = krow * (NCOL * 2) + ((c ^ swz_w<BCR>(krow)) << 4) + ((ncol & 7) << 1);
-      const int b1 = (krow + 4) * (NCOL * 2) + ((c ^ swz_w<BCR>(krow + 4)) << 4) + ((ncol & 7) << 1);
-      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b0));
-      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b1));
-      const short __attribute__((ext_vector_type(8))) both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      bfr[ni] = __builtin_bit_cast(uint4, both);
-    }
-    const uint4 m7 = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      if (PART && mi >= mact) break;
+      for (int mi = 0; mi < MI; ++mi) {
+        if (PART && mi >= mact) break;
+        const int row = wm * (16 * MI) + mi * 16 + s;
+        af[mi] = sA[row * XR + (SBK == 64 ? ks * 4 + g : g ^ swz4(row))];
+      }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[ni]),
-                                                              __builtin_bit_cast(bf16x8, af[mi]), acc[mi][ni], 0, 0, 0);
-        qs[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[ni] & m7),
-                                                             __builtin_bit_cast(bf16x8, af[mi] & m7), qs[mi][ni], 0, 0, 0);
+        // transposing read: lane L of a 16-lane group receives W[k0 .. k0+3][n + L]
+        const int krow = ks * 32 + 8 * g + (s >> 2);
+        const int ncol = wn * (16 * NI) + ni * 16 + 4 * (s & 3);
+        const int c = ncol >> 3;
+        const int b0 = krow * (NCOL * 2) + ((c ^ swz_w<BCR>(krow)) << 4) + ((ncol & 7) << 1);
+        const int b1 = (krow + 4) * (NCOL * 2) + ((c ^ swz_w<BCR>(krow + 4)) << 4) + ((ncol & 7) << 1);
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b0));
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(sB + b1));
+        const short __attribute__((ext_vector_type(8))) both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        bfr[ni] = __builtin_bit_cast(uint4, both);
+      }
+      const uint4 m7 = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        if (PART && mi >= mact) break;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[ni]),
+                                                                __builtin_bit_cast(bf16x8, af[mi]), acc[mi][ni], 0, 0, 0);
+          qs[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[ni] & m7),
+                                                               __builtin_bit_cast(bf16x8, af[mi] & m7), qs[mi][ni], 0, 0, 0);
+        }
       }
     }
   };
 
-  const int nk = (d + kBK - 1) / kBK;
+  const int nk = (d + SBK - 1) / SBK;  // stages
+  const int nsteps = nk * (SBK / 32);  // 32-wide MFMA k-steps, M of the bound
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t)
     if (t < nk) issue(t);
@@ -402,7 +413,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
 
   // ---- epilogue: clean logit (+ bias), softplus, H and the bound ------------------
   // Bound of |acc_mfma - acc_canon|: KB * (Q + S) (see the file header).
-  const float KB = 100.0f * 0x1.0p-24f * (1.0f + 256.0f * 0x1.0p-24f * (float)nk) * 1.004f;
+  const float KB = 100.0f * 0x1.0p-24f * (1.0f + 256.0f * 0x1.0p-24f * (float)nsteps) * 1.004f;
   // noise of this lane's (token, expert) entries, all loads in flight together
   constexpr int NE = NOISY ? NI / 2 : NI;  // 16-expert groups per lane
   float epsv[MI][NE][4];
