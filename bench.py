@@ -58,6 +58,9 @@ def parse():
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into --traffic-json")
     ap.add_argument("--stats-report", metavar="KERNEL_STATS_CSV",
                     help="print a rocprofv3 --stats kernel_stats.csv as a markdown table")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="time the vendor GEMM library (torch.matmul / torch.bmm, bf16) on dense and uniformly "
+                         "batched GEMMs with the workload's expert-layer shapes, as a point of comparison")
     return ap.parse_args()
 
 
@@ -441,8 +444,53 @@ def run_config(args, name):
     torch.cuda.empty_cache()
 
 
+def library_gemm(name, iters):
+    """Dense and uniformly batched bf16 GEMMs of the workload's expert layers through the vendor library
+    (torch.matmul / torch.bmm): M = T * k rows, layer 1 [M, d] x [d, f], layer 2 [M, f] x [f, d]; batched:
+    E segments of M / E rows, each against its own weight matrix. A reference point for the grouped GEMM,
+    which does the same work on ragged segments with the row gather, activation and gate fused."""
+    import torch
+    from synthetic.configs import CONFIGS
+
+    cfg = CONFIGS[name]
+    if cfg.dtype != "bf16":
+        sys.exit(f"--library-gemm: {name} is not a bf16 workload")
+    dev = torch.device("cuda:0")
+    M, E, d, f = cfg.T * cfg.k, cfg.E, cfg.d_model, cfg.d_ff
+    shapes = [(f"dense layer 1: [{M}, {d}] x [{d}, {f}]", (M, d), (d, f)),
+              (f"dense layer 2: [{M}, {f}] x [{f}, {d}]", (M, f), (f, d)),
+              (f"batched layer 1: {E} x [{M // E}, {d}] x [{d}, {f}]", (E, M // E, d), (E, d, f)),
+              (f"batched layer 2: {E} x [{M // E}, {f}] x [{f}, {d}]", (E, M // E, f), (E, f, d))]
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    print(f"library GEMMs, {name} shapes, bf16 in / bf16 out, {iters} back-to-back calls each")
+    print("| GEMM | ms | TFLOP/s | fraction of 2.5 PFLOP/s |")
+    print("|---|---:|---:|---:|")
+    for label, sa, sb in shapes:
+        a = torch.randn(sa, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        b = (torch.randn(sb, generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16).contiguous()
+        fn = (lambda: torch.bmm(a, b)) if a.dim() == 3 else (lambda: torch.matmul(a, b))
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        flops = 2.0 * M * d * f
+        print(f"| {label} | {ms:.3f} | {flops / ms / 1e9:.0f} | {flops / ms / 1e9 / 2500:.3f} |", flush=True)
+        del a, b
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
+    if args.library_gemm:
+        library_gemm(DEFAULT_CONFIG if args.config == "all" else args.config, args.steps)
+        return
     if args.stats_report:
         stats_report(args.stats_report)
         return
