@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdMiscArgs b) {
     const uint4* o = reinterpret_cast<const uint4*>(b.o) + (int64_t)slot * (b.d / 8);
     uint4* dO = reinterpret_cast<uint4*>(b.dO) + (int64_t)slot * (b.d / 8);
     for (int c = lane; c < b.d / 8; c += 64) {
-      const uint4 vy = dy[c], vo = o[c];
+      const uint4 vy = dy[c], vo = load_nt(o + c);  // o and dO rows: streamed once
       const uint32_t wy[4] = {vy.x, vy.y, vy.z, vy.w}, wo[4] = {vo.x, vo.y, vo.z, vo.w};
       uint32_t out[4];
 #pragma unroll
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdMiscArgs b) {
         dot = __builtin_fmaf(y1, bf16_hi(wo[q]), dot);
         out[q] = pack_bf16x2(g * y0, g * y1);
       }
-      dO[c] = uint4{out[0], out[1], out[2], out[3]};
+      store_nt(dO + c, uint4{out[0], out[1], out[2], out[3]});
     }
   } else {
     const float* dy = static_cast<const float*>(b.dy) + t * b.d;

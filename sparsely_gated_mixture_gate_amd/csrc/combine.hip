@@ -10,7 +10,8 @@
 // the token's k slots and gates (cached, shared by the row's threads),
 // gathers the k expert-output chunks, accumulates in fp32 with fma in slot
 // order and stores once. HBM-bound: 2d bytes read per kept assignment plus
-// 2d bytes written per token (bf16).
+// 2d bytes written per token (bf16). Expert-output rows are read once and the
+// output written once, both with the non-temporal hint.
 #include "common.h"
 
 namespace moe {
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     const int32_t slot = slot_dest[t * k + s];
     if (slot < 0) continue;
     const float g = gate[t * k + s];
-    const uint4 v = yp[(int64_t)slot * chunks_per_row + c];
+    const uint4 v = load_nt(yp + (int64_t)slot * chunks_per_row + c);
     if constexpr (BF16) {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     o.z = __float_as_uint(acc[2]);
     o.w = __float_as_uint(acc[3]);
   }
-  y[i] = o;
+  store_nt(y + i, o);
 }
 
 }  // namespace

@@ -306,7 +306,7 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const uint4* __restri
   const int64_t r = i / chunks_per_row;
   if (r >= offsets[E]) return;
   const int64_t c = i - r * chunks_per_row;
-  xp[i] = x[(int64_t)row_src[r] * chunks_per_row + c];
+  store_nt(xp + i, load_nt(x + (int64_t)row_src[r] * chunks_per_row + c));  // each row streamed once
 }
 
 }  // namespace

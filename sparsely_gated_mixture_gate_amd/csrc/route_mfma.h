@@ -318,8 +318,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     for (int i = 0; i < NR; ++i) {
       if (!act[i]) continue;
       const uint32_t dst = lds0 + (uint32_t)((st * CH + i * 512 + wave * 64) * 16);
-      if (isA[i])
-        load_to_lds(__builtin_amdgcn_readfirstlane(dst), voff[i] + kt * SBK * 2, rsX, 0);
+      if (isA[i])  // token rows: read by this block alone, once (non-temporal)
+        load_to_lds_nt(__builtin_amdgcn_readfirstlane(dst), voff[i] + kt * SBK * 2, rsX, 0);
       else
         load_to_lds(__builtin_amdgcn_readfirstlane(dst), voff[i] + kt * SBK * NCOL * 2, rsW, 0);
     }
