@@ -255,7 +255,12 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   constexpr int F_CH = F_WCH + F_XCH;            // chunks per fallback stage
   constexpr int F_NR = (F_CH + 511) / 512;
   constexpr int F_STAGES = F_FREE / (F_CH * 16) < 8 ? F_FREE / (F_CH * 16) : 8;
-  constexpr int SMEM = SMEM0 > OFF_CV + F_STAGES * F_CH * 16 ? SMEM0 : OFF_CV + F_STAGES * F_CH * 16;
+  constexpr int SMEM_R = SMEM0 > OFF_CV + F_STAGES * F_CH * 16 ? SMEM0 : OFF_CV + F_STAGES * F_CH * 16;
+  // The candidate chains stage their operands from OFF_CV + 4 KB on, in whatever LDS
+  // the occupancy leaves: up to 152 KB for a block alone on its CU, else 77 KB (two
+  // blocks per CU).
+  constexpr int SMEM_F = SMEM0 > 80 * 1024 ? 152 * 1024 : 77 * 1024;
+  constexpr int SMEM = SMEM_R > SMEM_F ? SMEM_R : SMEM_F;
   static_assert(F_WCH % 64 == 0 && F_STAGES >= 3 && F_NR <= 5 && NR <= 5 &&
                     SMEM + 1024 <= 160 * 1024,
                 "LDS");
@@ -266,6 +271,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   __shared__ int nflag_s;
   __shared__ int fb_full_s;  // the candidate pairs do not fit: the block recomputes whole rows
   __shared__ int np_s;       // candidate pairs of the block
+  __shared__ int tslot_s[kTok];  // token row of each x-row slot of a staging round
+  __shared__ int rnd_s[2];       // end of the staging round's pairs, its token count
   char* smem = reinterpret_cast<char*>(smem_u4);
   float* Hs = reinterpret_cast<float*>(smem);
   float* cand_v = reinterpret_cast<float*>(smem + OFF_CV);
@@ -793,22 +800,23 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     // c >= V - B, so an expert with v_e < V - 2B has c_e < V - B and cannot be in
     // the canonical top-KK. Only the other experts (the candidates) need their
     // canonical chains; the rest keep their MFMA logits, which then enter only the
-    // softmax sums. The (token, candidate) pairs are listed in token order, their
-    // x rows and weight columns gathered into LDS as fp32 by all threads, and each
-    // chain run by one thread from LDS (one fma per step), in rounds of as many
-    // pairs as the LDS holds. The
-    // forced fallback, and blocks with more pairs than threads (or than 16 rounds),
-    // recompute whole rows instead (below).
+    // softmax sums. The (token, candidate) pairs are listed in token order; in rounds
+    // of as many as the LDS holds, each round's token rows and the pairs' weight
+    // columns are gathered into LDS as fp32 by all threads (a token's row once, however
+    // many of its pairs the round holds), and each chain is run by one thread from LDS
+    // (one fma per step). The forced fallback, and blocks with more pairs than threads
+    // (or than about 16 rounds), recompute whole rows instead (below).
     int* pair_tok = reinterpret_cast<int*>(smem + OFF_CV);  // [512] token row of each pair
-    int* pair_e = pair_tok + 512;                            // [512] its expert
-    constexpr int OFF_ST = OFF_CV + 4096;                    // staged operands, one block per pair
+    int* pair_e = pair_tok + 512;                            // [512] its expert (| x-row slot << 16)
+    constexpr int OFF_ST = OFF_CV + 4096;                    // staged operands
     static_assert(OFF_WM - OFF_CV >= 4096 && SMEM >= OFF_ST, "candidate lists");
-    constexpr int NROW = NOISY ? 3 : 2;                      // x row, gate column (, noise column)
-    // pair block: NROW rows of d floats, padded to 4 dwords mod 64 so that the
-    // chains' 16-byte reads (one pair per lane) fall on distinct banks
-    const int pb_dw = NROW * d;
-    const int pb = 4 * (pb_dw + ((4 - pb_dw % 64) + 64) % 64);
-    const int maxp = (SMEM - OFF_ST) / pb;
+    constexpr int NW = NOISY ? 2 : 1;                        // weight columns per pair: gate (, noise)
+    // x-row slots (d floats) and pair blocks (NW * d floats), each padded to 4 dwords
+    // mod 64 so that the chains' 16-byte reads (one pair per lane) fall on distinct banks
+    const int xb = 4 * (d + ((4 - d % 64) + 64) % 64);
+    const int wb = 4 * (NW * d + ((4 - (NW * d) % 64) + 64) % 64);
+    const int cap = SMEM - OFF_ST;
+    const int maxp = (cap - xb) / wb;  // pairs of a single token that one round holds
     int* resi = reinterpret_cast<int*>(res);
     // candidates of flagged token q (lane = expert), in expert order; with emit, their
     // pairs are written from the token's list offset on; returns the count
@@ -862,46 +870,73 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
       for (int q = wave; q < nflag; q += 8) candidates(q, true);
       __syncthreads();
       const int n8 = d / 8;
-      for (int p0 = 0; p0 < np; p0 += maxp) {
-        const int pr = min(maxp, np - p0);
-        // gather: item (pair, 8 consecutive k) -> one 16-byte x load and 8 (16) weight
-        // loads, widened to fp32
-        auto gather = [&](int it) {
-          const int pl = it / n8, j8 = it - (it / n8) * n8;
-          const int m = pair_tok[p0 + pl], e = pair_e[p0 + pl];
-          float* blk = reinterpret_cast<float*>(smem + OFF_ST + pl * pb) + 8 * j8;
-          const uint4 xv = *reinterpret_cast<const uint4*>(a.x + (t0 + m) * d + 8 * j8);
-          const uint16_t* __restrict__ w = a.wcat + (size_t)(8 * j8) * NCOL + (NOISY ? 64 * (e >> 5) + (e & 31) : e);
-          uint32_t wg[8], wn[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            wg[u] = w[(size_t)u * NCOL];
-            if constexpr (NOISY) wn[u] = w[(size_t)u * NCOL + 32];
+      for (int p0 = 0; p0 < np;) {
+        // the round: pairs p0 .. p1 - 1, as many as fit with their nt token rows
+        if (tid == 0) {
+          int p = p0, nt = 0, last = -1;
+          while (p < np) {
+            const int m = pair_tok[p];
+            const int nt2 = nt + (m != last ? 1 : 0);
+            if (p > p0 && nt2 * xb + (p + 1 - p0) * wb > cap) break;
+            if (m != last) tslot_s[nt] = m;
+            pair_e[p] = (pair_e[p] & 0xFFFF) | ((nt2 - 1) << 16);
+            nt = nt2;
+            last = m;
+            ++p;
           }
-          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+          rnd_s[0] = p;
+          rnd_s[1] = nt;
+        }
+        __syncthreads();
+        const int p1 = rnd_s[0], nt = rnd_s[1], pr = p1 - p0;
+        const int pbase = OFF_ST + nt * xb;
+        // gather: item (x-row slot, 8 consecutive k) -> one 16-byte x load; item (pair,
+        // 8 consecutive k) -> 8 (16) weight loads; widened to fp32
+        auto gather = [&](int it) {
+          if (it < nt * n8) {
+            const int sl = it / n8, j8 = it - sl * n8;
+            float* blk = reinterpret_cast<float*>(smem + OFF_ST + sl * xb) + 8 * j8;
+            const uint4 xv = *reinterpret_cast<const uint4*>(a.x + (t0 + tslot_s[sl]) * d + 8 * j8);
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            *reinterpret_cast<float4*>(blk + 4 * h) = float4{bf16_lo(xw[2 * h]), bf16_hi(xw[2 * h]),
-                                                             bf16_lo(xw[2 * h + 1]), bf16_hi(xw[2 * h + 1])};
-            *reinterpret_cast<float4*>(blk + d + 4 * h) = float4{bf16_to_f32(wg[4 * h]), bf16_to_f32(wg[4 * h + 1]),
-                                                                 bf16_to_f32(wg[4 * h + 2]), bf16_to_f32(wg[4 * h + 3])};
-            if constexpr (NOISY)
-              *reinterpret_cast<float4*>(blk + 2 * d + 4 * h) = float4{bf16_to_f32(wn[4 * h]), bf16_to_f32(wn[4 * h + 1]),
-                                                                       bf16_to_f32(wn[4 * h + 2]), bf16_to_f32(wn[4 * h + 3])};
+            for (int h = 0; h < 2; ++h)
+              *reinterpret_cast<float4*>(blk + 4 * h) = float4{bf16_lo(xw[2 * h]), bf16_hi(xw[2 * h]),
+                                                               bf16_lo(xw[2 * h + 1]), bf16_hi(xw[2 * h + 1])};
+          } else {
+            const int i2 = it - nt * n8;
+            const int pl = i2 / n8, j8 = i2 - pl * n8;
+            const int e = pair_e[p0 + pl] & 0xFFFF;
+            float* blk = reinterpret_cast<float*>(smem + pbase + pl * wb) + 8 * j8;
+            const uint16_t* __restrict__ w = a.wcat + (size_t)(8 * j8) * NCOL + (NOISY ? 64 * (e >> 5) + (e & 31) : e);
+            uint32_t wg[8], wn[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              wg[u] = w[(size_t)u * NCOL];
+              if constexpr (NOISY) wn[u] = w[(size_t)u * NCOL + 32];
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              *reinterpret_cast<float4*>(blk + 4 * h) = float4{bf16_to_f32(wg[4 * h]), bf16_to_f32(wg[4 * h + 1]),
+                                                               bf16_to_f32(wg[4 * h + 2]), bf16_to_f32(wg[4 * h + 3])};
+              if constexpr (NOISY)
+                *reinterpret_cast<float4*>(blk + d + 4 * h) = float4{bf16_to_f32(wn[4 * h]), bf16_to_f32(wn[4 * h + 1]),
+                                                                     bf16_to_f32(wn[4 * h + 2]), bf16_to_f32(wn[4 * h + 3])};
+            }
           }
         };
-        const int nit = pr * n8;
+        const int nit = (nt + pr) * n8;
         for (int it = tid; it < nit; it += 1024) {  // two items per pass, their loads in flight together
           gather(it);
           if (it + 512 < nit) gather(it + 512);
         }
         __syncthreads();
         if (tid < pr) {
-          const int m = pair_tok[p0 + tid], e = pair_e[p0 + tid];
+          const int m = pair_tok[p0 + tid], pe = pair_e[p0 + tid];
+          const int e = pe & 0xFFFF;
           const int64_t t = t0 + m;
-          const float4* bx = reinterpret_cast<const float4*>(smem + OFF_ST + tid * pb);
-          const float4* bw = bx + d / 4;
-          const float4* bn = bx + d / 2;
+          const float4* bx = reinterpret_cast<const float4*>(smem + OFF_ST + (pe >> 16) * xb);
+          const float4* bw = reinterpret_cast<const float4*>(smem + pbase + tid * wb);
+          const float4* bn = bw + d / 4;
           float acc = 0.0f, accn = 0.0f;
 #pragma unroll 8
           for (int j4 = 0; j4 < d / 4; ++j4) {
@@ -930,6 +965,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
           }
         }
         __syncthreads();  // the staging area is refilled by the next round
+        p0 = p1;
       }
     } else {
       constexpr int TPR = 512 / NCOL;  // token slots
