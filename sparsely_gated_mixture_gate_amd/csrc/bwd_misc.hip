@@ -26,6 +26,7 @@
 //   dx         per token: sum of its kept rows of dXp (the dispatch's adjoint)
 //              + dclean_t W_gate^T (+ du_t W_noise^T), fp32, stored once
 #include "common.h"
+#include "stream_io.h"
 #include "route_tail.h"
 
 namespace moe {

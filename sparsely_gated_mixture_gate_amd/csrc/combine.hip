@@ -13,6 +13,7 @@
 // 2d bytes written per token (bf16). Expert-output rows are read once and the
 // output written once, both with the non-temporal hint.
 #include "common.h"
+#include "stream_io.h"
 
 namespace moe {
 namespace {

@@ -12,20 +12,6 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// 16-byte loads and stores with the non-temporal hint, for rows that a kernel
-// streams through once (row gathers, the combine): the data is not kept in the
-// caches for reuse. On MI355X a row-gather copy of 268 MB each way runs at
-// 5.8-5.9 TB/s with both hints against 4.0-4.1 TB/s with plain accesses.
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_nt(const uint4* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return uint4{v[0], v[1], v[2], v[3]};
-}
-__device__ __forceinline__ void store_nt(uint4* p, const uint4& v) {
-  const u32x4_t w = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
-}
-
 // Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest, ties to even:
 // one v_cvt_pk_bf16_f32 on gfx950 (the default round mode is nearest-even).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

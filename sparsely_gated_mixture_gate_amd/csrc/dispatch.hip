@@ -30,6 +30,7 @@
 //           whole rows, fully coalesced writes (not needed by the bf16 forward
 //           path, whose expert GEMM gathers its rows from x).
 #include "common.h"
+#include "stream_io.h"
 #include "route_tail.h"
 
 namespace moe {
