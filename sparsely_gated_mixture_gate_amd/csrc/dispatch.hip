@@ -61,13 +61,18 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
     return;
   }
   extern __shared__ int hist[];
+  const int64_t base = (int64_t)blockIdx.x * kChunk;
+  int eid[kChunk / 256];  // all loads in flight before the histogram updates
+#pragma unroll
+  for (int q = 0; q < kChunk / 256; ++q) {
+    const int64_t a = base + q * 256 + threadIdx.x;
+    eid[q] = a < n ? idx[walk_pos(a, tl)] : -1;
+  }
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kChunk;
-  for (int i = threadIdx.x; i < kChunk; i += 256) {
-    const int64_t a = base + i;
-    if (a < n) atomicAdd(&hist[idx[walk_pos(a, tl)]], 1);
-  }
+#pragma unroll
+  for (int q = 0; q < kChunk / 256; ++q)
+    if (eid[q] >= 0) atomicAdd(&hist[eid[q]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) blk_cnt[(int64_t)e * nb + blockIdx.x] = hist[e];
 }
@@ -161,6 +166,16 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
                                                             uint4* __restrict__ y_zero, int y_chunks,
                                                             const DispatchLaunch so) {
   extern __shared__ int wcnt[];  // [4 waves][E] running counts; SCAN: then base [E], segment starts [E + 1]
+  // this thread's four expert ids, loaded first so that they arrive under the prefix work
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t base = (int64_t)blockIdx.x * kChunk + wave * 256;
+  int eid[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t a = base + q * 64 + lane;  // walk position
+    eid[q] = (blockIdx.x < (unsigned)nb && a < n) ? idx[walk_pos(a, so)] : 0;
+  }
   for (int i = threadIdx.x; i < 4 * E; i += 256) wcnt[i] = 0;
   int* const base_s = wcnt + 4 * E;
   int* const off_s = base_s + E;
@@ -171,12 +186,12 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
     for (int e = threadIdx.x; e < E; e += 256) {
       const int32_t* row = blk_base + (int64_t)e * nb;
       int before = 0, tot = 0;
-      for (int b0 = 0; b0 < nb; b0 += 8) {
-        int32_t c[8];
+      for (int b0 = 0; b0 < nb; b0 += 16) {  // 16 loads in flight
+        int32_t c[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) c[u] = b0 + u < nb ? row[b0 + u] : 0;
+        for (int u = 0; u < 16; ++u) c[u] = b0 + u < nb ? row[b0 + u] : 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           before += b0 + u < (int)blockIdx.x ? c[u] : 0;
           tot += c[u];
         }
@@ -240,16 +255,13 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
     }
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int64_t base = (int64_t)blockIdx.x * kChunk + wave * 256;
   int ex[4], loc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t a = base + q * 64 + lane;  // walk position
     const bool valid = a < n;
-    const int e = valid ? idx[walk_pos(a, so)] : 0;
+    const int e = valid ? eid[q] : 0;
     uint64_t same = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
