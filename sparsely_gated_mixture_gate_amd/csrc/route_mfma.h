@@ -813,8 +813,11 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     constexpr int NW = NOISY ? 2 : 1;                        // weight columns per pair: gate (, noise)
     // x-row slots (d floats) and pair blocks (NW * d floats), each padded to 4 dwords
     // mod 64 so that the chains' 16-byte reads (one pair per lane) fall on distinct banks
+    // (noisy: the noise column starts nof dwords into the pair block, 32 mod 64, so the two
+    // lanes that run a pair's gate and noise chains read distinct banks)
+    const int nof = NOISY ? ((d + 63) / 64) * 64 + 32 : 0;
     const int xb = 4 * (d + ((4 - d % 64) + 64) % 64);
-    const int wb = 4 * (NW * d + ((4 - (NW * d) % 64) + 64) % 64);
+    const int wb = 4 * ((nof + d) + ((4 - (nof + d) % 64) + 64) % 64);
     const int cap = SMEM - OFF_ST;
     const int maxp = (cap - xb) / wb;  // pairs of a single token that one round holds
     int* resi = reinterpret_cast<int*>(res);
@@ -877,7 +880,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
           while (p < np) {
             const int m = pair_tok[p];
             const int nt2 = nt + (m != last ? 1 : 0);
-            if (p > p0 && nt2 * xb + (p + 1 - p0) * wb > cap) break;
+            if (p > p0 && (nt2 * xb + (p + 1 - p0) * wb > cap || p - p0 >= 512 / NW)) break;  // NW threads per pair
             if (m != last) tslot_s[nt] = m;
             pair_e[p] = (pair_e[p] & 0xFFFF) | ((nt2 - 1) << 16);
             nt = nt2;
@@ -919,8 +922,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
               *reinterpret_cast<float4*>(blk + 4 * h) = float4{bf16_to_f32(wg[4 * h]), bf16_to_f32(wg[4 * h + 1]),
                                                                bf16_to_f32(wg[4 * h + 2]), bf16_to_f32(wg[4 * h + 3])};
               if constexpr (NOISY)
-                *reinterpret_cast<float4*>(blk + d + 4 * h) = float4{bf16_to_f32(wn[4 * h]), bf16_to_f32(wn[4 * h + 1]),
-                                                                     bf16_to_f32(wn[4 * h + 2]), bf16_to_f32(wn[4 * h + 3])};
+                *reinterpret_cast<float4*>(blk + nof + 4 * h) = float4{bf16_to_f32(wn[4 * h]), bf16_to_f32(wn[4 * h + 1]),
+                                                                       bf16_to_f32(wn[4 * h + 2]), bf16_to_f32(wn[4 * h + 3])};
             }
           }
         };
@@ -930,14 +933,16 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
           if (it + 512 < nit) gather(it + 512);
         }
         __syncthreads();
-        if (tid < pr) {
-          const int m = pair_tok[p0 + tid], pe = pair_e[p0 + tid];
+        // one chain per thread (noisy: threads 2p and 2p + 1 run pair p's gate and noise
+        // chains side by side, then the gate thread takes the noise sum from its neighbour)
+        if (tid < NW * pr) {
+          const int pl = NOISY ? tid >> 1 : tid;
+          const int m = pair_tok[p0 + pl], pe = pair_e[p0 + pl];
           const int e = pe & 0xFFFF;
           const int64_t t = t0 + m;
           const float4* bx = reinterpret_cast<const float4*>(smem + OFF_ST + (pe >> 16) * xb);
-          const float4* bw = reinterpret_cast<const float4*>(smem + pbase + tid * wb);
-          const float4* bn = bw + d / 4;
-          float acc = 0.0f, accn = 0.0f;
+          const float4* bw = reinterpret_cast<const float4*>(smem + pbase + pl * wb + (NOISY ? (tid & 1) * nof * 4 : 0));
+          float acc = 0.0f;
 #pragma unroll 8
           for (int j4 = 0; j4 < d / 4; ++j4) {
             const float4 xv = bx[j4], wv = bw[j4];
@@ -945,22 +950,20 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
             acc = __builtin_fmaf(xv.y, wv.y, acc);
             acc = __builtin_fmaf(xv.z, wv.z, acc);
             acc = __builtin_fmaf(xv.w, wv.w, acc);
-            if constexpr (NOISY) {
-              const float4 nv = bn[j4];
-              accn = __builtin_fmaf(xv.x, nv.x, accn);
-              accn = __builtin_fmaf(xv.y, nv.y, accn);
-              accn = __builtin_fmaf(xv.z, nv.z, accn);
-              accn = __builtin_fmaf(xv.w, nv.w, accn);
-            }
           }
-          float cl = acc;
-          if (a.bias) cl = cl + a.bias[e];
           if constexpr (NOISY) {
-            const float sp = canon_softplus(accn);
-            Hs[m * HS + e] = __builtin_fmaf(a.noise[t * E + e], sp, cl);
-            a.CL[t * a.lpad + e] = cl;
-            a.SG[t * a.lpad + e] = sp;
+            const float accn = __shfl_xor(acc, 1);  // the noise chain of the pair
+            if ((tid & 1) == 0) {
+              float cl = acc;
+              if (a.bias) cl = cl + a.bias[e];
+              const float sp = canon_softplus(accn);
+              Hs[m * HS + e] = __builtin_fmaf(a.noise[t * E + e], sp, cl);
+              a.CL[t * a.lpad + e] = cl;
+              a.SG[t * a.lpad + e] = sp;
+            }
           } else {
+            float cl = acc;
+            if (a.bias) cl = cl + a.bias[e];
             Hs[m * HS + e] = cl;
           }
         }
