@@ -59,6 +59,7 @@ struct FusedArgs {
   int d, E, k, renormalize, nblk, force_fallback, lpad, tpb;
   const uint16_t* x;
   const uint16_t* wcat;
+  const uint16_t* wt;  // noisy: wcat transposed, [NCOL][d]
   const float* bias;
   const float* noise;
   int32_t* topk_idx;
@@ -910,12 +911,23 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
             const int pl = i2 / n8, j8 = i2 - pl * n8;
             const int e = pair_e[p0 + pl] & 0xFFFF;
             float* blk = reinterpret_cast<float*>(smem + pbase + pl * wb) + 8 * j8;
-            const uint16_t* __restrict__ w = a.wcat + (size_t)(8 * j8) * NCOL + (NOISY ? 64 * (e >> 5) + (e & 31) : e);
             uint32_t wg[8], wn[8];
+            if constexpr (NOISY) {  // contiguous rows of the transposed copy: 16 bytes each of the two columns
+              const size_t cg = 64 * (e >> 5) + (e & 31);
+              const uint4 g = *reinterpret_cast<const uint4*>(a.wt + cg * d + 8 * j8);
+              const uint4 q = *reinterpret_cast<const uint4*>(a.wt + (cg + 32) * d + 8 * j8);
+              const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, qw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              wg[u] = w[(size_t)u * NCOL];
-              if constexpr (NOISY) wn[u] = w[(size_t)u * NCOL + 32];
+              for (int u = 0; u < 4; ++u) {
+                wg[2 * u] = gw[u] & 0xFFFFu;
+                wg[2 * u + 1] = gw[u] >> 16;
+                wn[2 * u] = qw[u] & 0xFFFFu;
+                wn[2 * u + 1] = qw[u] >> 16;
+              }
+            } else {
+              const uint16_t* __restrict__ w = a.wcat + (size_t)(8 * j8) * NCOL + e;
+#pragma unroll
+              for (int u = 0; u < 8; ++u) wg[u] = w[(size_t)u * NCOL];
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {

@@ -17,10 +17,12 @@ namespace {
 
 // bf16 weight copy [d][ncol]: gate only: column c = expert c; noisy: block q of
 // 64 columns = gate columns of experts 32q .. 32q+31, then their noise columns.
-// Zero past E.
+// Zero past E. Noisy: also its transpose [ncol][d] after it (wt), so that the
+// fallback gathers a candidate's gate and noise columns as contiguous rows.
 __global__ __launch_bounds__(256) void route_wcat_kernel(const uint16_t* __restrict__ wg,
                                                          const uint16_t* __restrict__ wn,
-                                                         uint16_t* __restrict__ wcat, int d, int E, int ncol) {
+                                                         uint16_t* __restrict__ wcat, uint16_t* __restrict__ wt,
+                                                         int d, int E, int ncol) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)d * ncol) return;
   const int64_t j = i / ncol;
@@ -31,7 +33,9 @@ __global__ __launch_bounds__(256) void route_wcat_kernel(const uint16_t* __restr
     e = 32 * (c >> 6) + (c & 31);
     if (c & 32) src = wn;
   }
-  wcat[i] = e < E ? src[j * E + e] : (uint16_t)0;
+  const uint16_t v = e < E ? src[j * E + e] : (uint16_t)0;
+  wcat[i] = v;
+  if (wt) wt[(int64_t)c * d + j] = v;
 }
 
 int fused_ep(int E) { return E <= 64 ? 64 : (E <= 128 ? 128 : 256); }
@@ -42,7 +46,7 @@ int fused_ep(int E) { return E <= 64 ? 64 : (E <= 128 ? 128 : 256); }
 bool route_fused_supported(int dtype, int E) { return dtype == 1 && E <= 256; }
 
 size_t route_wcat_elems(int d, int E, bool noisy) {
-  return (size_t)d * moe::fused_ep(E) * (noisy ? 2 : 1);
+  return (size_t)d * moe::fused_ep(E) * (noisy ? 4 : 1);  // noisy: [d][2 EP] and its transpose
 }
 
 // Tokens per block of the certified gate: a block holds most of a CU's LDS, so
@@ -74,7 +78,8 @@ hipError_t launch_route_fused(const RouteLaunch& a, bool noisy, int force_fallba
   if (noisy || a.E != EP) {
     hipLaunchKernelGGL(route_wcat_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(a.w_gate),
-                       static_cast<const uint16_t*>(noisy ? a.w_noise : nullptr), a.wcat, a.d, a.E, ncol);
+                       static_cast<const uint16_t*>(noisy ? a.w_noise : nullptr), a.wcat,
+                       noisy ? a.wcat + (size_t)a.d * ncol : nullptr, a.d, a.E, ncol);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     wcat = a.wcat;
@@ -91,6 +96,7 @@ hipError_t launch_route_fused(const RouteLaunch& a, bool noisy, int force_fallba
   fa.lpad = lpad;
   fa.x = static_cast<const uint16_t*>(a.x);
   fa.wcat = wcat;
+  fa.wt = noisy ? a.wcat + (size_t)a.d * ncol : nullptr;
   fa.bias = a.gate_bias;
   fa.noise = a.noise;
   fa.topk_idx = a.topk_idx;
