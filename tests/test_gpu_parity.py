@@ -400,12 +400,15 @@ def test_zero_gate_ties_and_identity_experts(moelib, dev):
     assert np.all(y[C:] == 0.0)
 
 
-@pytest.mark.parametrize("name,over", [("switch_top1", dict(T=2048)), ("gshard_top2", dict(T=1024))])
+@pytest.mark.parametrize("name,over", [("switch_top1", dict(T=2048)), ("gshard_top2", dict(T=1024)),
+                                       ("noisy_top4", dict(T=2048, d_model=128, d_ff=64))])
 def test_twin_gate_columns(moelib, dev, name, over):
     """Every gate column has an identical twin (column 2j+1 = column 2j), so every
     token's top-(k+1) ties exactly: no token is certified, and each block
     recomputes the tied candidates of all its tokens canonically (over a hundred
-    (token, expert) pairs, several LDS rounds). Ties go to the lower expert index."""
+    (token, expert) pairs, several LDS rounds). Ties go to the lower expert index.
+    The noisy case twins the noise columns too and draws no noise (eps = 0), so its
+    logits tie the same way and every pair runs its gate and noise chains."""
     from sparsely_gated_mixture_gate_amd.buffers import to_device
 
     cfg = scaled(CONFIGS[name], **over)
@@ -413,6 +416,11 @@ def test_twin_gate_columns(moelib, dev, name, over):
     wg = inp["w_gate"].copy()
     wg[:, 1::2] = wg[:, 0::2]
     inp["w_gate"] = wg
+    if inp.get("w_noise") is not None:
+        wn = inp["w_noise"].copy()
+        wn[:, 1::2] = wn[:, 0::2]
+        inp["w_noise"] = wn
+        inp["noise"] = np.zeros_like(inp["noise"])
     spec = oracle.LayerSpec.of(cfg, capacity=-1)
     r = oracle.route(spec, inp)
     C = oracle.capacity(cfg.T, cfg.E, cfg.k, cfg.capacity_factor, -1)
