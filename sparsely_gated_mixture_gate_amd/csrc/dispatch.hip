@@ -152,10 +152,10 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
 // SCAN = false: blk_base holds the exclusive prefixes of the block counts along
 // each expert and offsets the segment starts (written by the scan kernel).
 // SCAN = true (small count tables): blk_base holds the raw block counts; every
-// rank block derives its own prefixes and the offsets from them, and one extra
-// block (blockIdx.x == nb, no ranks) writes counts_kept, offsets, the FFN tile
-// map and the losses (as the scan kernel would), so no separate scan launch is
-// needed and that work runs beside the ranks instead of before block 0's.
+// rank block derives its own prefixes and the offsets from them, one extra block
+// (blockIdx.x == nb, no ranks) writes counts_kept, offsets and the FFN tile map,
+// and a second (nb + 1) the losses (as the scan kernel would), so no separate scan
+// launch is needed and that work runs beside the ranks instead of before block 0's.
 template <bool SCAN>
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __restrict__ idx, int64_t n, int k,
                                                             int E, int nbits, int nb, int64_t C,
@@ -182,6 +182,11 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
   if constexpr (SCAN) {
     __shared__ int64_t sw[16];
     __shared__ double sh[16];
+    if (blockIdx.x == nb + 1) {  // the second extra block: the losses, beside the other blocks
+      if (so.route_tail && so.aux_out)
+        tail::aux_block<256>(so.counts_routed, so.red, E, so.T, so.k, so.noisy, so.aux_out, sh);
+      return;
+    }
     // per expert: counts of the blocks before this one, and the total
     for (int e = threadIdx.x; e < E; e += 256) {
       const int32_t* row = blk_base + (int64_t)e * nb;
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
     }
     if (threadIdx.x == 255) off_s[E] = (int)incl;
     __syncthreads();
-    if (blockIdx.x == nb) {  // the extra block: offsets, kept counts, tile map and losses, no ranks
+    if (blockIdx.x == nb) {  // the extra block: offsets, kept counts and tile map, no ranks
       for (int e = threadIdx.x; e <= E; e += 256) so.offsets[e] = off_s[e];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -249,8 +254,6 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __res
         }
         if (threadIdx.x == 255) so.tile_start[E] = (int32_t)tincl;
       }
-      if (so.route_tail && so.aux_out)
-        tail::aux_block<256>(so.counts_routed, so.red, E, so.T, so.k, so.noisy, so.aux_out, sh);
       return;
     }
   }
@@ -352,7 +355,7 @@ hipError_t launch_dispatch(const DispatchLaunch& a, hipStream_t s) {
   const int y_chunks = a.d * (a.dtype == 1 ? 2 : 4) / 16;
   if (scan_in_rank) {
     // nb rank blocks and one block for offsets, tile map and losses, which then run side by side
-    hipLaunchKernelGGL(dispatch_rank_kernel<true>, dim3(nb + 1), dim3(256), sizeof(int) * (6 * a.E + 1), s, a.topk_idx,
+    hipLaunchKernelGGL(dispatch_rank_kernel<true>, dim3(nb + 2), dim3(256), sizeof(int) * (6 * a.E + 1), s, a.topk_idx,
                        n, a.k, a.E, nbits, nb, a.C, a.blk_cnt, a.offsets, a.slot_dest, a.row_src,
                        static_cast<uint4*>(a.y_zero), y_chunks, a);
   } else {
