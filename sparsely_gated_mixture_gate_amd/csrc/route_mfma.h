@@ -895,7 +895,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
         const int p1 = rnd_s[0], nt = rnd_s[1], pr = p1 - p0;
         const int pbase = OFF_ST + nt * xb;
         // gather: item (x-row slot, 8 consecutive k) -> one 16-byte x load; item (pair,
-        // 8 consecutive k) -> 8 (16) weight loads; widened to fp32
+        // 8 consecutive k) -> 8 weight loads (noisy: two 16-byte loads from the transposed
+        // copy, gate and noise column); widened to fp32
         auto gather = [&](int it) {
           if (it < nt * n8) {
             const int sl = it / n8, j8 = it - sl * n8;
