@@ -38,7 +38,8 @@
 // One block = 64 tokens, 512 threads (8 waves):
 //   GEMM: x tile [64][BK] and weight tile [BK][NCOL] per stage in an LDS ring
 //   (direct-to-LDS buffer loads): BK = 64 and up to 4 stages for NCOL <= 128
-//   (each token's 128 bytes of a stage are one unswizzled L2 request), else
+//   (each token's 128 bytes of a stage are one L2 request in lane order; each
+//   load takes 8 rows 8 apart into a 1 KB block padded by 16 bytes), else
 //   BK = 32 and up to 8 stages (x rows XOR-swizzled); v_mfma_f32_16x16x32_bf16 with
 //   swapped operands (lane = 4 consecutive columns of one token); noisy: each
 //   wave's 64 columns are 32 experts' gate columns and the same experts' noise
@@ -210,13 +211,20 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   constexpr int MI = 4 / WM_W;             // 16-token MFMA tiles per wave
   constexpr int BCR = NCOL / 8;            // 16-byte chunks per weight row
   // k per LDS stage: 64 where the weight tile stays small (then the x rows of a stage are
-  // 128 bytes, loaded unswizzled so that each is one L2 request), else 32 (x rows swizzled)
+  // 128 bytes, loaded in lane order so that each is one L2 request), else 32 (x rows swizzled)
   constexpr int SBK = NCOL <= 128 ? 64 : 32;
   constexpr int XR = SBK / 8;              // x chunks per row per stage
   constexpr int A_CH = kTok * XR;          // x chunks per stage
   constexpr int B_CH = SBK * BCR;          // weight chunks per stage
   constexpr int CH = A_CH + B_CH;
   constexpr int NR = (CH + 511) / 512;     // load rounds per stage
+  // 64-wide stages: the x rows of a stage are one load round, each wave's load taking the
+  // 8 rows w, w + 8, ..., w + 56 (each row's 128 bytes in lane order) into a 1 KB block of
+  // its own padded to 1040 bytes, so the 16 rows of an MFMA operand read fall 16 bytes
+  // apart in the banks instead of on the same ones
+  constexpr int APAD = SBK == 64 ? 8 : 0;  // uint4 of padding per stage
+  constexpr int STG = CH + APAD;           // uint4 per stage
+  static_assert(SBK != 64 || A_CH == 512, "x rows of a 64-wide stage: one load round");
   constexpr int HS = EP + 1;               // LDS row stride of the logit tile (floats)
   constexpr int EPW = EP / 8;              // experts per wave in the scan
   constexpr int KS = KK < 8 ? KK : 8;      // selectable slots
@@ -224,9 +232,9 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
   static_assert(CH % 64 == 0 && WN_W * WM_W == 8 && MI >= 1 && (!NOISY || NI == 4), "shape");
   // GEMM ring depth: as many stages as fit beside the other LDS use (at most 8 of 32 k, 4 of 64 k)
   constexpr int kMaxStages = SBK == 64 ? 4 : 8;
-  constexpr int kStages = (144 * 1024) / (CH * 16) < kMaxStages ? (144 * 1024) / (CH * 16) : kMaxStages;
+  constexpr int kStages = (144 * 1024) / (STG * 16) < kMaxStages ? (144 * 1024) / (STG * 16) : kMaxStages;
   static_assert(kStages >= 3, "ring");
-  constexpr int RING = kStages * CH * 16;
+  constexpr int RING = kStages * STG * 16;
   // After the GEMM the ring's LDS holds: the logit tile H and the per-token
   // results (live to the end), then the selection state, which the fallback's
   // own ring overwrites (the selection is redone after it).
@@ -308,7 +316,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     isA[i] = (i * 512 + wave * 64) < A_CH;
     ld += act[i] ? 1 : 0;
     if (c < A_CH) {
-      const int row = c / XR, p = c % XR;
+      const int row = SBK == 64 ? wave + 8 * (lane >> 3) : c / XR;
+      const int p = SBK == 64 ? lane & 7 : c % XR;
       const int pc = SBK == 64 ? p : p ^ swz4(row);
       voff[i] = min(row, rows - 1) * d * 2 + (pc << 4);  // rows past T: clamped, never stored
     } else {
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       if (!act[i]) continue;
-      const uint32_t dst = lds0 + (uint32_t)((st * CH + i * 512 + wave * 64) * 16);
+      const uint32_t dst = lds0 + (uint32_t)(st * STG * 16 + (SBK == 64 && isA[i] ? wave * 1040 : (i * 512 + wave * 64 + APAD) * 16));
       if (isA[i])  // token rows: read by this block alone, once (non-temporal)
         load_to_lds_nt(__builtin_amdgcn_readfirstlane(dst), voff[i] + kt * SBK * 2, rsX, 0);
       else
@@ -361,8 +370,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
 
   auto compute = [&](int st, auto part_c) {
     constexpr bool PART = decltype(part_c)::value;
-    const uint4* sA = &smem_u4[st * CH];
-    lds_char* sB = (lds_char*)(&smem_u4[st * CH + A_CH]);
+    const uint4* sA = &smem_u4[st * STG];
+    lds_char* sB = (lds_char*)(&smem_u4[st * STG + A_CH + APAD]);
 #pragma unroll
     for (int ks = 0; ks < SBK / 32; ++ks) {  // one 32-wide MFMA k-step each
       add_q(part_c);
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
       for (int mi = 0; mi < MI; ++mi) {
         if (PART && mi >= mact) break;
         const int row = wm * (16 * MI) + mi * 16 + s;
-        af[mi] = sA[row * XR + (SBK == 64 ? ks * 4 + g : g ^ swz4(row))];
+        af[mi] = SBK == 64 ? sA[(row & 7) * 65 + (row >> 3) * 8 + ks * 4 + g] : sA[row * XR + (g ^ swz4(row))];
       }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
