@@ -109,8 +109,13 @@ __device__ __forceinline__ float fast_normal_cdf(float z) {
   const float q = p * t * fast_exp(-(a * a));  // erfc(a)
   return z >= 0.0f ? 1.0f - 0.5f * q : 0.5f * q;
 }
+// Weight tile: even XOR inside the row's BCR chunks, from k mod 4 (the four rows of one
+// transposing read) and bit 3 of k (rows 8 apart, read by the neighbouring 16-lane group).
+// With 8 chunks (128-byte rows) bit 3 flips chunk bit 1, which moves the odd groups onto
+// the 16 bank slots the even groups leave free.
 template <int BCR>
-__device__ __forceinline__ int swz_w(int k) {  // weight tile: even XOR inside the row's BCR chunks
+__device__ __forceinline__ int swz_w(int k) {
+  if constexpr (BCR == 8) return (2 * (k & 3)) ^ (((k >> 3) & 1) << 1);
   return (2 * ((k & 3) | (((k >> 3) & 1) << 2))) & (BCR - 2);
 }
 
