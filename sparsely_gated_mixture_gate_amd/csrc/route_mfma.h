@@ -826,13 +826,17 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
     constexpr int OFF_ST = OFF_CV + 4096;                    // staged operands
     static_assert(OFF_WM - OFF_CV >= 4096 && SMEM >= OFF_ST, "candidate lists");
     constexpr int NW = NOISY ? 2 : 1;                        // weight columns per pair: gate (, noise)
-    // x-row slots (d floats) and pair blocks (NW * d floats), each padded to 4 dwords
-    // mod 64 so that the chains' 16-byte reads (one pair per lane) fall on distinct banks
-    // (noisy: the noise column starts nof dwords into the pair block, 32 mod 64, so the two
-    // lanes that run a pair's gate and noise chains read distinct banks)
-    const int nof = NOISY ? ((d + 63) / 64) * 64 + 32 : 0;
-    const int xb = 4 * (d + ((4 - d % 64) + 64) % 64);
-    const int wb = 4 * ((nof + d) + ((4 - (nof + d) % 64) + 64) % 64);
+    // x-row slots (d fp32) and pair blocks (NW * d weights), each padded to 16 bytes mod
+    // 256 so that the chains' 16-byte reads (one pair per lane) fall on distinct banks.
+    // WB16 (noisy gate): the weights stay bf16 and are widened to fp32 (exactly) in the
+    // chains, one shift or mask per k, so a round holds about twice the pairs; that extra
+    // op lengthens a chain by about 1.45x, which pays where rounds are short (the noise
+    // column starts nofb bytes into the pair block, 128 mod 256, so the two lanes that run
+    // a pair's gate and noise chains read distinct banks). Plain gates stage fp32 weights.
+    constexpr bool WB16 = NOISY;
+    const int nofb = NOISY ? ((2 * d + 255) / 256) * 256 + 128 : 0;
+    const int xb = 4 * d + ((16 - (4 * d) % 256) + 256) % 256;
+    const int wb = WB16 ? (nofb + 2 * d) + ((16 - (nofb + 2 * d) % 256) + 256) % 256 : xb;
     const int cap = SMEM - OFF_ST;
     const int maxp = (cap - xb) / wb;  // pairs of a single token that one round holds
     int* resi = reinterpret_cast<int*>(res);
@@ -910,7 +914,8 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
         const int pbase = OFF_ST + nt * xb;
         // gather: item (x-row slot, 8 consecutive k) -> one 16-byte x load; item (pair,
         // 8 consecutive k) -> 8 weight loads (noisy: two 16-byte loads from the transposed
-        // copy, gate and noise column); widened to fp32
+        // copy, gate and noise column); x widened to fp32, weights as bf16 (WB16) or fp32,
+        // k ascending
         auto gather = [&](int it) {
           if (it < nt * n8) {
             const int sl = it / n8, j8 = it - sl * n8;
@@ -925,32 +930,22 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
             const int i2 = it - nt * n8;
             const int pl = i2 / n8, j8 = i2 - pl * n8;
             const int e = pair_e[p0 + pl] & 0xFFFF;
-            float* blk = reinterpret_cast<float*>(smem + pbase + pl * wb) + 8 * j8;
-            uint32_t wg[8], wn[8];
+            char* blk = smem + pbase + pl * wb + (WB16 ? 16 : 32) * j8;
             if constexpr (NOISY) {  // contiguous rows of the transposed copy: 16 bytes each of the two columns
               const size_t cg = 64 * (e >> 5) + (e & 31);
-              const uint4 g = *reinterpret_cast<const uint4*>(a.wt + cg * d + 8 * j8);
-              const uint4 q = *reinterpret_cast<const uint4*>(a.wt + (cg + 32) * d + 8 * j8);
-              const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, qw[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                wg[2 * u] = gw[u] & 0xFFFFu;
-                wg[2 * u + 1] = gw[u] >> 16;
-                wn[2 * u] = qw[u] & 0xFFFFu;
-                wn[2 * u + 1] = qw[u] >> 16;
-              }
+              *reinterpret_cast<uint4*>(blk) = *reinterpret_cast<const uint4*>(a.wt + cg * d + 8 * j8);
+              *reinterpret_cast<uint4*>(blk + nofb) = *reinterpret_cast<const uint4*>(a.wt + (cg + 32) * d + 8 * j8);
             } else {
               const uint16_t* __restrict__ w = a.wcat + (size_t)(8 * j8) * NCOL + e;
+              uint32_t wg[8];
 #pragma unroll
               for (int u = 0; u < 8; ++u) wg[u] = w[(size_t)u * NCOL];
-            }
+              static_assert(!WB16, "plain gates stage fp32 weights");
+              float* fb = reinterpret_cast<float*>(blk);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              *reinterpret_cast<float4*>(blk + 4 * h) = float4{bf16_to_f32(wg[4 * h]), bf16_to_f32(wg[4 * h + 1]),
-                                                               bf16_to_f32(wg[4 * h + 2]), bf16_to_f32(wg[4 * h + 3])};
-              if constexpr (NOISY)
-                *reinterpret_cast<float4*>(blk + nof + 4 * h) = float4{bf16_to_f32(wn[4 * h]), bf16_to_f32(wn[4 * h + 1]),
-                                                                       bf16_to_f32(wn[4 * h + 2]), bf16_to_f32(wn[4 * h + 3])};
+              for (int h = 0; h < 2; ++h)
+                *reinterpret_cast<float4*>(fb + 4 * h) = float4{bf16_to_f32(wg[4 * h]), bf16_to_f32(wg[4 * h + 1]),
+                                                                bf16_to_f32(wg[4 * h + 2]), bf16_to_f32(wg[4 * h + 3])};
             }
           }
         };
@@ -968,15 +963,28 @@ __global__ __launch_bounds__(512) void route_fused_kernel(FusedArgs a) {
           const int e = pe & 0xFFFF;
           const int64_t t = t0 + m;
           const float4* bx = reinterpret_cast<const float4*>(smem + OFF_ST + (pe >> 16) * xb);
-          const float4* bw = reinterpret_cast<const float4*>(smem + pbase + pl * wb + (NOISY ? (tid & 1) * nof * 4 : 0));
+          const char* bwc = smem + pbase + pl * wb + (NOISY ? (tid & 1) * nofb : 0);
           float acc = 0.0f;
-#pragma unroll 8
-          for (int j4 = 0; j4 < d / 4; ++j4) {
-            const float4 xv = bx[j4], wv = bw[j4];
-            acc = __builtin_fmaf(xv.x, wv.x, acc);
-            acc = __builtin_fmaf(xv.y, wv.y, acc);
-            acc = __builtin_fmaf(xv.z, wv.z, acc);
-            acc = __builtin_fmaf(xv.w, wv.w, acc);
+#pragma unroll 4
+          for (int j8 = 0; j8 < d / 8; ++j8) {  // k = 8 j8 .. 8 j8 + 7 in order: low half, then high half of each word
+            const float4 x0 = bx[2 * j8], x1 = bx[2 * j8 + 1];
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            float ws[8];
+            if constexpr (WB16) {
+              const uint4 wv = reinterpret_cast<const uint4*>(bwc)[j8];
+              const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                ws[2 * u] = __uint_as_float(ww[u] << 16);
+                ws[2 * u + 1] = __uint_as_float(ww[u] & 0xFFFF0000u);
+              }
+            } else {
+              const float4 w0 = reinterpret_cast<const float4*>(bwc)[2 * j8], w1 = reinterpret_cast<const float4*>(bwc)[2 * j8 + 1];
+              ws[0] = w0.x; ws[1] = w0.y; ws[2] = w0.z; ws[3] = w0.w;
+              ws[4] = w1.x; ws[5] = w1.y; ws[6] = w1.z; ws[7] = w1.w;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(xs[u], ws[u], acc);
           }
           if constexpr (NOISY) {
             const float accn = __shfl_xor(acc, 1);  // the noise chain of the pair
